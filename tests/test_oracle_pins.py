@@ -1,0 +1,395 @@
+"""Pins of the CPU oracle to facts fixed outside itself.
+
+Every oracle function is checked against something it does not share code
+with: an independent library routine (torch's float8_e4m3fn codec, torch's
+scaled_dot_product_attention in float64), closed forms, the worked example
+of the Lecture 33 page (§2.2: token 37 -> logical block 2, offset 5 ->
+physical block 142), and invariants the pages state (paged result equals the
+contiguous result; shared prefix blocks give the same output as private
+copies; block ids can be permuted freely).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle
+
+pytestmark = pytest.mark.filterwarnings("ignore::UserWarning")
+
+
+# ----------------------------------------------------------------------------
+# helpers (test-side; none of them calls the oracle)
+# ----------------------------------------------------------------------------
+
+def to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def bf16_bits_to_f64(b: np.ndarray) -> np.ndarray:
+    return torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+
+
+def fp8_codes_to_f64(c: np.ndarray) -> np.ndarray:
+    return torch.from_numpy(c).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def torch_fp8_quantize(x: np.ndarray, kv_scale: float) -> np.ndarray:
+    """Library route: y = x * (1/s) in fp32, saturate to +-448, torch RNE cast."""
+    inv = np.float32(1.0) / np.float32(kv_scale)
+    with np.errstate(over="ignore", invalid="ignore"):
+        y = (x.astype(np.float32) * inv).astype(np.float32)
+        y = np.where(np.isnan(y), y, np.clip(y, -448.0, 448.0)).astype(np.float32)
+    return torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def scatter_to_pool(seqs_kv, tables, num_blocks, hkv, d, dtype):
+    """Place each sequence's logical [L, Hkv, d] rows into a pool through its
+    table by reshaping the padded sequence into [nblk, 16, Hkv, d] pages."""
+    pool = np.zeros((num_blocks, 16, hkv, d), dtype=dtype)
+    for kv, table in zip(seqs_kv, tables):
+        L = kv.shape[0]
+        nblk = -(-L // 16)
+        pad = np.zeros((nblk * 16, hkv, d), dtype=dtype)
+        pad[:L] = kv
+        pool[np.asarray(table[:nblk])] = pad.reshape(nblk, 16, hkv, d)
+    return pool.reshape(num_blocks * 16, hkv, d)
+
+
+def sdpa_reference(q_f64, k_f64, v_f64, scale, mask=None):
+    """torch SDPA in float64: q [Hq, n, d], k/v [Hkv, L, d] expanded to Hq by
+    repeating each KV head G times (query head h reads KV head h // G)."""
+    hq = q_f64.shape[0]
+    g = hq // k_f64.shape[0]
+    k = torch.from_numpy(k_f64).repeat_interleave(g, dim=0)
+    v = torch.from_numpy(v_f64).repeat_interleave(g, dim=0)
+    q = torch.from_numpy(q_f64)
+    m = None if mask is None else torch.from_numpy(mask)
+    return F.scaled_dot_product_attention(q[None], k[None], v[None], attn_mask=m,
+                                          scale=scale)[0].numpy()
+
+
+def random_case(rng, S, hq, hkv, d, lens, num_blocks, storage, kv_scale=0.05):
+    """Random paged problem; returns host arrays in storage form plus the
+    float64 logical KV each sequence sees (decoded with the library)."""
+    tables = []
+    perm = rng.permutation(num_blocks)
+    cursor = 0
+    maxb = max(-(-L // 16) for L in lens)
+    bt = np.full((S, maxb), -1, dtype=np.int32)
+    for i, L in enumerate(lens):
+        nb = -(-L // 16)
+        t = perm[cursor:cursor + nb]
+        cursor += nb
+        bt[i, :nb] = t
+        tables.append(t)
+    k_logical = [rng.standard_normal((L, hkv, d)).astype(np.float32) for L in lens]
+    v_logical = [rng.standard_normal((L, hkv, d)).astype(np.float32) for L in lens]
+    if storage == "f32":
+        ks, vs = k_logical, v_logical
+        kdec = [x.astype(np.float64) for x in ks]
+        vdec = [x.astype(np.float64) for x in vs]
+        sdt = np.float32
+    elif storage == "bf16":
+        ks = [to_bf16_bits(x) for x in k_logical]
+        vs = [to_bf16_bits(x) for x in v_logical]
+        kdec = [bf16_bits_to_f64(x) for x in ks]
+        vdec = [bf16_bits_to_f64(x) for x in vs]
+        sdt = np.uint16
+    else:
+        kb = [bf16_bits_to_f64(to_bf16_bits(x)).astype(np.float32) for x in k_logical]
+        vb = [bf16_bits_to_f64(to_bf16_bits(x)).astype(np.float32) for x in v_logical]
+        ks = [torch_fp8_quantize(x, kv_scale) for x in kb]
+        vs = [torch_fp8_quantize(x, kv_scale) for x in vb]
+        kdec = [fp8_codes_to_f64(x) * np.float64(np.float32(kv_scale)) for x in ks]
+        vdec = [fp8_codes_to_f64(x) * np.float64(np.float32(kv_scale)) for x in vs]
+        sdt = np.uint8
+    kpool = scatter_to_pool(ks, tables, num_blocks, hkv, d, sdt)
+    vpool = scatter_to_pool(vs, tables, num_blocks, hkv, d, sdt)
+    qf = rng.standard_normal((S, hq, d)).astype(np.float32)
+    if storage == "f32":
+        q = qf
+        qdec = qf.astype(np.float64)
+    else:
+        q = to_bf16_bits(qf)
+        qdec = bf16_bits_to_f64(q)
+    return dict(q=q, qdec=qdec, kpool=kpool, vpool=vpool, bt=bt, lens=np.array(lens, np.int32),
+                kdec=kdec, vdec=vdec, kv_scale=np.float32(kv_scale))
+
+
+# ----------------------------------------------------------------------------
+# fp8 E4M3FN codec
+# ----------------------------------------------------------------------------
+
+def test_fp8_value_matches_library_for_all_codes():
+    lib = fp8_codes_to_f64(np.arange(256, dtype=np.uint8))
+    mine = np.array([oracle.fp8_value(c) for c in range(256)])
+    nan = np.isnan(lib)
+    assert np.array_equal(nan, np.isnan(mine))
+    assert nan.sum() == 2  # S.1111.111 only
+    assert np.array_equal(lib[~nan], mine[~nan])
+    # signed zero is kept
+    assert math.copysign(1.0, oracle.fp8_value(0x80)) == -1.0
+
+
+def test_fp8_encode_worked_values():
+    assert oracle.fp8_encode(1.0) == 0x38
+    assert oracle.fp8_encode(448.0) == 0x7E
+    assert oracle.fp8_encode(1e9) == 0x7E           # saturates
+    assert oracle.fp8_encode(float("inf")) == 0x7E
+    assert oracle.fp8_encode(-float("inf")) == 0xFE
+    assert oracle.fp8_encode(2.0 ** -9) == 0x01      # smallest subnormal
+    assert oracle.fp8_encode(2.0 ** -10) == 0x00     # tie -> even (zero)
+    assert oracle.fp8_encode(3 * 2.0 ** -10) == 0x02  # tie between 1 and 2 -> 2
+    assert oracle.fp8_encode(-0.0) == 0x80
+    assert oracle.fp8_encode(float("nan")) & 0x7F == 0x7F
+
+
+def test_fp8_quantize_exhaustive_over_bf16_inputs():
+    """All 65,536 bf16 bit patterns, times 1/0.05 in fp32, against torch's
+    float8_e4m3fn cast of the saturated value."""
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    x = bf16_bits_to_f64(bits).astype(np.float32)
+    lib = torch_fp8_quantize(x, 0.05)
+    mine = np.array([oracle.fp8_quantize(float(v), 0.05) for v in x], dtype=np.uint8)
+    isnan = np.isnan(x)
+    assert np.array_equal(mine[~isnan], lib[~isnan])
+    assert np.all((mine[isnan] & 0x7F) == 0x7F)
+    assert np.array_equal(mine[isnan] >> 7, (bits[isnan] >> 15).astype(np.uint8))
+
+
+# ----------------------------------------------------------------------------
+# cache write
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("storage", ["f32", "bf16", "fp8"])
+def test_reshape_writes_exactly_the_mapped_slots(storage):
+    rng = np.random.default_rng(11)
+    T, hkv, d, slots = 7, 2, 64, 8 * 16
+    kf = rng.standard_normal((T, hkv, d)).astype(np.float32)
+    vf = rng.standard_normal((T, hkv, d)).astype(np.float32)
+    if storage == "f32":
+        k, v, cdt = kf, vf, np.float32
+    else:
+        k, v = to_bf16_bits(kf), to_bf16_bits(vf)
+        cdt = np.uint16 if storage == "bf16" else np.uint8
+    kc0 = rng.integers(0, 255, size=(slots, hkv, d * np.dtype(cdt).itemsize), dtype=np.uint8)
+    vc0 = rng.integers(0, 255, size=(slots, hkv, d * np.dtype(cdt).itemsize), dtype=np.uint8)
+    kc = kc0.copy().view(cdt)
+    vc = vc0.copy().view(cdt)
+    slot_mapping = np.array([37, -1, 5, 127, 0, -7, 64], dtype=np.int64)
+    oracle.reshape_and_cache(k, v, kc, vc, slot_mapping, kv_scale=0.05)
+    written = slot_mapping[slot_mapping >= 0]
+    untouched = np.setdiff1d(np.arange(slots), written)
+    assert np.array_equal(kc.view(np.uint8)[untouched], kc0[untouched])
+    assert np.array_equal(vc.view(np.uint8)[untouched], vc0[untouched])
+    for n, s in enumerate(slot_mapping):
+        if s < 0:
+            continue
+        if storage == "fp8":
+            kx = bf16_bits_to_f64(k[n]).astype(np.float32)
+            vx = bf16_bits_to_f64(v[n]).astype(np.float32)
+            assert np.array_equal(kc[s], torch_fp8_quantize(kx, 0.05))
+            assert np.array_equal(vc[s], torch_fp8_quantize(vx, 0.05))
+        else:
+            assert np.array_equal(kc[s], k[n])
+            assert np.array_equal(vc[s], v[n])
+
+
+# ----------------------------------------------------------------------------
+# decode attention
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("storage,hq,hkv,d", [
+    ("f32", 4, 2, 64), ("bf16", 28, 4, 128), ("bf16", 8, 8, 64), ("bf16", 32, 8, 128),
+    ("fp8", 32, 8, 128), ("bf16", 6, 2, 64),
+])
+def test_decode_equals_sdpa_over_contiguous_kv(storage, hq, hkv, d):
+    rng = np.random.default_rng(hq * 100 + d)
+    lens = [1, 15, 16, 17, 37, 64, 100]
+    c = random_case(rng, len(lens), hq, hkv, d, lens, 64, storage)
+    scale = 1.0 / math.sqrt(d)
+    out = oracle.decode(c["q"], c["kpool"], c["vpool"], c["bt"], c["lens"], scale,
+                        kv_scale=c["kv_scale"])
+    for i, L in enumerate(lens):
+        ref = sdpa_reference(c["qdec"][i][:, None, :], c["kdec"][i].transpose(1, 0, 2).copy(),
+                             c["vdec"][i].transpose(1, 0, 2).copy(), scale)[:, 0, :]
+        np.testing.assert_allclose(out[i], ref, rtol=0, atol=1e-12)
+
+
+def test_decode_sample_selection_matches_full():
+    rng = np.random.default_rng(3)
+    lens = [20, 33, 48]
+    c = random_case(rng, 3, 8, 2, 64, lens, 16, "bf16")
+    full = oracle.decode(c["q"], c["kpool"], c["vpool"], c["bt"], c["lens"], 0.125)
+    part = oracle.decode(c["q"], c["kpool"], c["vpool"], c["bt"], c["lens"], 0.125,
+                         sel_seq=[2, 0, 1], sel_head=[7, 3, 0])
+    assert np.array_equal(part, np.stack([full[2, 7], full[0, 3], full[1, 0]]))
+
+
+def _tiny_f32(L, hq=2, hkv=1, d=8, nblocks=8, seed=0):
+    rng = np.random.default_rng(seed)
+    nb = -(-L // 16)
+    table = rng.permutation(nblocks)[:nb].astype(np.int32)
+    k = rng.standard_normal((nblocks * 16, hkv, d)).astype(np.float32)
+    v = rng.standard_normal((nblocks * 16, hkv, d)).astype(np.float32)
+    q = rng.standard_normal((1, hq, d)).astype(np.float32)
+    return q, k, v, table[None, :], np.array([L], np.int32)
+
+
+def test_closed_form_single_token_returns_its_value():
+    q, k, v, bt, lens = _tiny_f32(1)
+    out = oracle.decode(q, k, v, bt, lens, 0.7)
+    slot = bt[0, 0] * 16
+    assert np.array_equal(out[0, 0], v[slot, 0].astype(np.float64))
+    assert np.array_equal(out[0, 1], v[slot, 0].astype(np.float64))
+
+
+def test_closed_form_zero_query_is_mean_of_values():
+    q, k, v, bt, lens = _tiny_f32(37)
+    q[:] = 0
+    out = oracle.decode(q, k, v, bt, lens, 1.0)
+    slots = np.array([bt[0, t // 16] * 16 + t % 16 for t in range(37)])
+    np.testing.assert_allclose(out[0, 0], v[slots, 0].astype(np.float64).mean(0), rtol=0, atol=1e-14)
+
+
+def test_closed_form_equal_keys_is_mean_and_equal_values_is_that_value():
+    q, k, v, bt, lens = _tiny_f32(50)
+    k[:] = k[0]
+    out = oracle.decode(q, k, v, bt, lens, 0.3)
+    slots = np.array([bt[0, t // 16] * 16 + t % 16 for t in range(50)])
+    np.testing.assert_allclose(out[0, 1], v[slots, 0].astype(np.float64).mean(0), rtol=0, atol=1e-14)
+    q, k, v, bt, lens = _tiny_f32(50, seed=4)
+    v[:] = v[3]
+    out = oracle.decode(q, k, v, bt, lens, 0.3)
+    np.testing.assert_allclose(out[0, 0], v[3, 0].astype(np.float64), rtol=0, atol=1e-14)
+
+
+def test_worked_example_token_37_reads_block_142_offset_5():
+    """Lecture 33 §2.2: token 37 lies in logical block 2 at offset 5; with
+    table[2] = 142 it is read from physical block 142, slot 142*16+5."""
+    d, hkv = 8, 1
+    table = np.array([[9, 77, 142, 3]], dtype=np.int32)
+    k = np.zeros((160 * 16, hkv, d), np.float32)
+    v = np.zeros((160 * 16, hkv, d), np.float32)
+    v[142 * 16 + 5, 0] = np.arange(1, d + 1)
+    q = np.zeros((1, 1, d), np.float32)
+    out = oracle.decode(q, k, v, table, np.array([38], np.int32), 1.0)
+    np.testing.assert_allclose(out[0, 0], np.arange(1, d + 1) / 38.0, rtol=0, atol=1e-15)
+    # the same value planted one slot off is not read as token 37
+    v[:] = 0
+    v[142 * 16 + 6, 0] = np.arange(1, d + 1)
+    out = oracle.decode(q, k, v, table, np.array([38], np.int32), 1.0)
+    assert np.all(out == 0)
+
+
+def test_permuting_physical_block_ids_changes_nothing():
+    rng = np.random.default_rng(5)
+    lens = [30, 70, 5]
+    c = random_case(rng, 3, 4, 2, 64, lens, 24, "bf16")
+    base = oracle.decode(c["q"], c["kpool"], c["vpool"], c["bt"], c["lens"], 0.125)
+    pi = rng.permutation(24)
+    kp = np.empty_like(c["kpool"].reshape(24, 16, 2, 64))
+    vp = np.empty_like(kp)
+    kp[pi] = c["kpool"].reshape(24, 16, 2, 64)
+    vp[pi] = c["vpool"].reshape(24, 16, 2, 64)
+    bt = np.where(c["bt"] >= 0, pi[np.maximum(c["bt"], 0)], -1).astype(np.int32)
+    moved = oracle.decode(c["q"], kp.reshape(-1, 2, 64), vp.reshape(-1, 2, 64), bt, c["lens"], 0.125)
+    assert np.array_equal(base, moved)
+
+
+def test_shared_block_equals_duplicated_block():
+    """[VM] §3.4: two tables pointing at one physical block (ref_cnt 2) give
+    the same result as each sequence owning an identical copy."""
+    rng = np.random.default_rng(6)
+    hkv, d = 2, 64
+    k = to_bf16_bits(rng.standard_normal((8 * 16, hkv, d)).astype(np.float32))
+    v = to_bf16_bits(rng.standard_normal((8 * 16, hkv, d)).astype(np.float32))
+    k[5 * 16:6 * 16] = k[2 * 16:3 * 16]
+    v[5 * 16:6 * 16] = v[2 * 16:3 * 16]
+    q = to_bf16_bits(rng.standard_normal((2, 4, d)).astype(np.float32))
+    lens = np.array([25, 20], np.int32)
+    shared = np.array([[2, 1], [2, 3]], np.int32)
+    private = np.array([[2, 1], [5, 3]], np.int32)
+    a = oracle.decode(q, k, v, shared, lens, 0.125)
+    b = oracle.decode(q, k, v, private, lens, 0.125)
+    assert np.array_equal(a, b)
+
+
+def test_unused_table_entries_are_never_read():
+    rng = np.random.default_rng(8)
+    c = random_case(rng, 2, 4, 2, 64, [17, 40], 8, "bf16")
+    a = oracle.decode(c["q"], c["kpool"], c["vpool"], c["bt"], c["lens"], 0.125)
+    bt = c["bt"].copy()
+    bt[0, 2:] = 10 ** 6  # far outside the pool: must stay unread
+    b = oracle.decode(c["q"], c["kpool"], c["vpool"], bt, c["lens"], 0.125)
+    assert np.array_equal(a, b)
+
+
+# ----------------------------------------------------------------------------
+# chunked prefill
+# ----------------------------------------------------------------------------
+
+def _prefill_case(rng, hist, n, hq=8, hkv=2, d=64, nblocks=64, storage="bf16"):
+    C = hist + n
+    c = random_case(rng, 1, hq, hkv, d, [C], nblocks, storage)
+    qf = rng.standard_normal((n, hq, d)).astype(np.float32)
+    q = qf if storage == "f32" else to_bf16_bits(qf)
+    qdec = q.astype(np.float64) if storage == "f32" else bf16_bits_to_f64(q)
+    return c, q, qdec, np.array([0, n], np.int32), np.array([C], np.int32)
+
+
+def test_prefill_without_history_is_causal_sdpa():
+    rng = np.random.default_rng(21)
+    c, q, qdec, qs, cl = _prefill_case(rng, 0, 40)
+    out = oracle.prefill(q, c["kpool"], c["vpool"], c["bt"], qs, cl, 0.125)
+    hq = q.shape[1]
+    g = hq // 2
+    k = torch.from_numpy(c["kdec"][0].transpose(1, 0, 2).copy()).repeat_interleave(g, 0)
+    v = torch.from_numpy(c["vdec"][0].transpose(1, 0, 2).copy()).repeat_interleave(g, 0)
+    ref = F.scaled_dot_product_attention(torch.from_numpy(qdec.transpose(1, 0, 2).copy())[None],
+                                         k[None], v[None], is_causal=True, scale=0.125)[0]
+    np.testing.assert_allclose(out, ref.numpy().transpose(1, 0, 2), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("storage", ["bf16", "fp8"])
+def test_prefill_with_history_is_masked_sdpa(storage):
+    rng = np.random.default_rng(22)
+    hist, n = 53, 30
+    c, q, qdec, qs, cl = _prefill_case(rng, hist, n, storage=storage)
+    out = oracle.prefill(q, c["kpool"], c["vpool"], c["bt"], qs, cl, 0.125, kv_scale=c["kv_scale"])
+    mask = np.arange(hist + n)[None, :] <= (hist + np.arange(n))[:, None]
+    ref = sdpa_reference(qdec.transpose(1, 0, 2).copy(), c["kdec"][0].transpose(1, 0, 2).copy(),
+                         c["vdec"][0].transpose(1, 0, 2).copy(), 0.125, mask=mask)
+    np.testing.assert_allclose(out, ref.transpose(1, 0, 2), rtol=0, atol=1e-12)
+
+
+def test_prefill_chunk_of_one_row_equals_decode():
+    rng = np.random.default_rng(23)
+    c, q, qdec, qs, cl = _prefill_case(rng, 70, 1)
+    a = oracle.prefill(q, c["kpool"], c["vpool"], c["bt"], qs, cl, 0.125)
+    b = oracle.decode(q, c["kpool"], c["vpool"], c["bt"], cl, 0.125)
+    assert np.array_equal(a, b)
+
+
+def test_prefill_two_requests_back_to_back():
+    """Rows of request r use request r's table and length only."""
+    rng = np.random.default_rng(24)
+    hq, hkv, d = 4, 2, 64
+    lens = [50, 20]
+    c = random_case(rng, 2, hq, hkv, d, lens, 16, "bf16")
+    n = [6, 3]
+    q = to_bf16_bits(rng.standard_normal((9, hq, d)).astype(np.float32))
+    qdec = bf16_bits_to_f64(q)
+    qs = np.array([0, 6, 9], np.int32)
+    out = oracle.prefill(q, c["kpool"], c["vpool"], c["bt"], qs, c["lens"], 0.125)
+    for r in range(2):
+        hist = lens[r] - n[r]
+        mask = np.arange(lens[r])[None, :] <= (hist + np.arange(n[r]))[:, None]
+        ref = sdpa_reference(qdec[qs[r]:qs[r + 1]].transpose(1, 0, 2).copy(),
+                             c["kdec"][r].transpose(1, 0, 2).copy(),
+                             c["vdec"][r].transpose(1, 0, 2).copy(), 0.125, mask=mask)
+        np.testing.assert_allclose(out[qs[r]:qs[r + 1]], ref.transpose(1, 0, 2), rtol=0, atol=1e-12)
