@@ -1,0 +1,207 @@
+#!/usr/bin/env python3
+"""Benchmark: one paged-attention step on one MI355X.
+
+A step is the whole hot path over one batch: the cache write of the step's
+new tokens (pa_reshape_and_cache), the decode attention of every sequence
+(pa_decode) and, for the mixed workloads, the chunked-prefill attention
+(pa_prefill_chunk).  Inputs are seeded synthetic tensors already resident in
+HBM before the timed region.
+
+    python bench.py [--steps K] [--warmup W] [--workload qwen7b] [--no-cpu-baseline]
+
+Prints one JSON line.  `value` is the effective KV bandwidth of the step: KV
+bytes the decode must read (each sequence's K and V rows, once) divided by
+the step time.  The roofline entry is for the decode launch (its two
+kernels), timed with HIP events on the stream the kernels run on.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+from paged_kv_cache_157_amd import binding
+from paged_kv_cache_157_amd.workload import CONFIGS, apply_cow, kv_bytes_per_token, make_step
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "paged decode attention: effective KV HBM GB/s (% of peak) and tokens/s, 1 GPU"
+HOST_CORE_SHARE = 16
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="qwen7b", choices=sorted(CONFIGS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic-json", default=os.path.join(os.path.dirname(__file__), "profiles",
+                                                           "traffic.json"),
+                    help="counter-measured HBM bytes per decode launch, if recorded")
+    return ap.parse_args()
+
+
+def algorithmic_bytes(cfg, step) -> dict:
+    """Bytes the decode launch must move: K/V rows once per sequence, q, out,
+    the table entries it reads and the lengths."""
+    L = step.plan.context_lens.astype(np.int64)
+    qb = 4 if cfg.q_dtype == "f32" else 2
+    kv = int(L.sum()) * kv_bytes_per_token(cfg)
+    q = cfg.num_seqs * cfg.num_q_heads * cfg.head_dim * qb
+    out = cfg.num_seqs * cfg.num_q_heads * cfg.head_dim * 4
+    tables = int(((L + 15) // 16).sum()) * 4 + 4 * cfg.num_seqs
+    return dict(kv=kv, total=kv + q + out + tables)
+
+
+def cpu_baseline(cfg, step) -> dict:
+    """The CPU oracle, as it stands, on a bounded sample of the same batch."""
+    import oracle  # test infrastructure: used only for this baseline leg
+
+    def host_bits(t):
+        if t.dtype == torch.float32:
+            return t.cpu().numpy()
+        if t.dtype == torch.bfloat16:
+            return t.view(torch.int16).cpu().numpy().view(np.uint16)
+        return t.view(torch.uint8).cpu().numpy()
+
+    def pool_rows(a):
+        return a.reshape(a.shape[0] * a.shape[1], a.shape[2], a.shape[3])
+
+    cores = min(HOST_CORE_SHARE, os.cpu_count() or 1)
+    kp = host_bits(step.k_cache)
+    vp = host_bits(step.v_cache)
+    q = host_bits(step.q)
+    L = step.plan.context_lens
+    order = np.argsort(-L)  # a deterministic sample: sequences in length order
+    budget_s, used = 15.0, 0.0
+    done_bytes = 0
+    n_seq = 0
+    t0 = time.time()
+    for i in order:
+        sel_seq = np.full(cfg.num_q_heads, i, np.int32)
+        sel_head = np.arange(cfg.num_q_heads, dtype=np.int32)
+        oracle.decode(q, pool_rows(kp), pool_rows(vp), step.plan.block_tables, L, cfg.scale,
+                      kv_scale=cfg.kv_scale, sel_seq=sel_seq, sel_head=sel_head,
+                      num_threads=cores)
+        done_bytes += int(L[i]) * kv_bytes_per_token(cfg)
+        n_seq += 1
+        used = time.time() - t0
+        if used > budget_s:
+            break
+    return dict(value=round(done_bytes / used / 1e9, 4), unit="GB/s", cores=cores, kind="oracle",
+                sample=f"{n_seq} of {cfg.num_seqs} sequences (longest first), all "
+                       f"{cfg.num_q_heads} heads, {used:.1f} s")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no "
+              "multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    binding.load()
+    cfg = CONFIGS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    step = make_step(cfg, dev)
+    out = torch.empty(step.q.shape, dtype=torch.float32, device=dev)
+    out_pre = None
+    if step.q_prefill is not None:
+        out_pre = torch.empty(step.q_prefill.shape, dtype=torch.float32, device=dev)
+    apply_cow(step)
+    torch.cuda.synchronize()
+
+    def run_step(ev=None):
+        binding.reshape_and_cache(step.k_new, step.v_new, step.k_cache, step.v_cache,
+                                  step.slot_mapping, kv_scale=cfg.kv_scale)
+        if out_pre is not None:
+            if ev is not None:
+                ev[2].record()
+            binding.prefill_chunk(out_pre, step.q_prefill, step.k_cache, step.v_cache,
+                                  step.prefill_table, step.prefill_query_start,
+                                  step.prefill_context, cfg.scale, kv_scale=cfg.kv_scale)
+            if ev is not None:
+                ev[3].record()
+        if ev is not None:
+            ev[0].record()
+        binding.decode(out, step.q, step.k_cache, step.v_cache, step.block_tables,
+                       step.context_lens, cfg.scale, partition_tokens=cfg.partition_tokens,
+                       kv_scale=cfg.kv_scale)
+        if ev is not None:
+            ev[1].record()
+
+    for _ in range(args.warmup):
+        run_step()
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        run_step(events[k])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    dec_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
+    pre_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in events])) if out_pre is not None \
+        else None
+
+    ab = algorithmic_bytes(cfg, step)
+    kv_gbs = ab["kv"] / (ms_per_step * 1e-3) / 1e9
+    achieved = ab["total"] / (dec_ms * 1e-3) / 1e9
+    traffic = None
+    if os.path.exists(args.traffic_json):
+        try:
+            rec = json.load(open(args.traffic_json)).get(cfg.name)
+            if rec:
+                traffic = rec.get("bytes_per_launch")
+        except (OSError, ValueError):
+            traffic = None
+
+    res = {
+        "metric": METRIC,
+        "value": round(kv_gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.cache_dtype,
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: {cfg.title}", "num_seqs": cfg.num_seqs,
+                   "q_heads": cfg.num_q_heads, "kv_heads": cfg.num_kv_heads,
+                   "head_dim": cfg.head_dim, "block_size": 16, "pool_blocks": cfg.num_blocks,
+                   "context_tokens": int(step.plan.context_lens.sum()),
+                   "new_tokens": int(len(step.plan.slot_mapping)), "seed": cfg.seed},
+        "pct_of_hbm_peak": round(100.0 * kv_gbs / HBM_PEAK_GBS, 2),
+        "tokens_per_s": round(cfg.num_seqs / (ms_per_step * 1e-3), 1),
+        "decode_us": round(dec_ms * 1e3, 2),
+        "decode_kv_gbs": round(ab["kv"] / (dec_ms * 1e-3) / 1e9, 2),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "kernel": "pa_decode (decode_kernel + decode_reduce)",
+                     "algorithmic_bytes_per_launch": ab["total"]},
+    }
+    if pre_ms is not None:
+        g = cfg.num_q_heads * cfg.head_dim * 4 * sum(
+            cfg.prefill_history + j + 1 for j in range(cfg.prefill_chunk))
+        res["prefill_us"] = round(pre_ms * 1e3, 2)
+        res["prefill_tflops"] = round(g / (pre_ms * 1e-3) / 1e12, 2)
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(cfg, step)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

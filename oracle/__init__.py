@@ -114,6 +114,7 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, scale, kv_scale=1.0,
     """
     S, hq, d = q.shape
     hkv = k_cache.shape[1]
+    kv_scale = float(np.float32(kv_scale))  # the scale is an fp32 value in the C ABI
     full = sel_seq is None
     if full:
         sel_seq = np.repeat(np.arange(S, dtype=np.int32), hq)
@@ -138,6 +139,7 @@ def prefill(q, k_cache, v_cache, block_tables, query_start, context_lens, scale,
     """Chunked-prefill attention for (row, head) pairs; returns float64 [n_sel, d]."""
     Tq, hq, d = q.shape
     hkv = k_cache.shape[1]
+    kv_scale = float(np.float32(kv_scale))  # the scale is an fp32 value in the C ABI
     full = sel_row is None
     if full:
         sel_row = np.repeat(np.arange(Tq, dtype=np.int32), hq)

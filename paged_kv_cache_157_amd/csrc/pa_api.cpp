@@ -1,0 +1,295 @@
+// pa_api.cpp -- C ABI of libpa (declared in include/pa.h): argument checks on
+// the host, workspace carving, and kernel launches.  No call allocates device
+// memory, synchronises the host or copies data back.
+#include "pa.h"
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+
+#include "pa_internal.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+pa_status fail(pa_status s, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+pa_status fail(pa_status s, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+pa_status ok()
+{
+    g_last_error[0] = '\0';
+    return PA_OK;
+}
+
+pa_status hip_fail(hipError_t e, const char *what)
+{
+    return fail(PA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Compute units of the current device (cached per device id).
+int device_cus()
+{
+    static std::mutex mu;
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return 256;
+    std::lock_guard<std::mutex> lock(mu);
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            n <= 0)
+            n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
+// Persistent decode grid: two work-groups per compute unit.
+int decode_grid() { return 2 * device_cus(); }
+
+pa_status check_shape(const pa_shape *s, bool need_tables)
+{
+    if (!s)
+        return fail(PA_ERR_INVALID, "shape is NULL");
+    if (s->num_seqs < 0)
+        return fail(PA_ERR_INVALID, "num_seqs < 0");
+    if (s->num_q_heads <= 0 || s->num_kv_heads <= 0)
+        return fail(PA_ERR_INVALID, "head counts must be positive");
+    if (s->num_q_heads % s->num_kv_heads != 0)
+        return fail(PA_ERR_INVALID, "num_q_heads %% num_kv_heads != 0 (%d, %d)", s->num_q_heads,
+                    s->num_kv_heads);
+    if (s->num_blocks <= 0)
+        return fail(PA_ERR_INVALID, "num_blocks must be positive");
+    if (s->num_blocks > (int64_t)1 << 31)
+        return fail(PA_ERR_UNSUPPORTED, "num_blocks above 2^31");
+    if (need_tables && s->max_blocks_per_seq <= 0)
+        return fail(PA_ERR_INVALID, "max_blocks_per_seq must be positive");
+    if (s->cache_dtype != PA_F32 && s->cache_dtype != PA_BF16 && s->cache_dtype != PA_FP8_E4M3)
+        return fail(PA_ERR_INVALID, "unknown cache_dtype %d", s->cache_dtype);
+    if (s->head_dim != 64 && s->head_dim != 128)
+        return fail(PA_ERR_UNSUPPORTED, "head_dim %d (64 or 128 are built)", s->head_dim);
+    if (s->cache_dtype == PA_FP8_E4M3 && !(s->kv_scale > 0.f && std::isfinite(s->kv_scale)))
+        return fail(PA_ERR_INVALID, "kv_scale must be finite and > 0 for an fp8 cache");
+    return PA_OK;
+}
+
+int q_dtype_for(int cache_dtype) { return cache_dtype == PA_F32 ? PA_F32 : PA_BF16; }
+
+float kv_scale_of(const pa_shape *s) { return s->cache_dtype == PA_FP8_E4M3 ? s->kv_scale : 1.f; }
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct DecodeLayout {
+    int64_t slots;
+    size_t acc_bytes, ml_bytes, lohi_bytes, total;
+};
+
+DecodeLayout decode_layout(const pa_shape *s)
+{
+    const int G = s->num_q_heads / s->num_kv_heads;
+    const int pb = s->partition_tokens > 0 ? s->partition_tokens / 16 : 0;
+    DecodeLayout L;
+    L.slots = pa::decode_partial_slots(s->num_seqs, s->num_kv_heads, s->max_blocks_per_seq, pb,
+                                       decode_grid());
+    L.acc_bytes = align256((size_t)L.slots * G * s->head_dim * sizeof(float));
+    L.ml_bytes = align256((size_t)L.slots * G * 2 * sizeof(float));
+    L.lohi_bytes = align256((size_t)s->num_seqs * s->num_kv_heads * 2 * sizeof(int32_t));
+    L.total = L.acc_bytes + L.ml_bytes + L.lohi_bytes;
+    return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *pa_status_string(pa_status s)
+{
+    switch (s) {
+    case PA_OK: return "ok";
+    case PA_ERR_INVALID: return "invalid argument";
+    case PA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case PA_ERR_WORKSPACE: return "workspace missing or too small";
+    case PA_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+const char *pa_last_error(void) { return g_last_error; }
+
+pa_status pa_reshape_and_cache(const void *k, const void *v, void *k_cache, void *v_cache,
+                               const int64_t *slot_mapping, int64_t num_tokens,
+                               int32_t src_dtype, const pa_shape *shape, void *stream)
+{
+    pa_status st = check_shape(shape, false);
+    if (st != PA_OK)
+        return st;
+    if (num_tokens < 0)
+        return fail(PA_ERR_INVALID, "num_tokens < 0");
+    if (src_dtype != q_dtype_for(shape->cache_dtype))
+        return fail(PA_ERR_UNSUPPORTED, "src_dtype %d cannot feed cache_dtype %d", src_dtype,
+                    shape->cache_dtype);
+    if (num_tokens == 0)
+        return ok();
+    if (!k || !v || !k_cache || !v_cache || !slot_mapping)
+        return fail(PA_ERR_INVALID, "NULL data pointer");
+    pa::ReshapeArgs a;
+    a.k = k;
+    a.v = v;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.slot_mapping = slot_mapping;
+    a.num_tokens = num_tokens;
+    a.num_slots = shape->num_blocks * 16;
+    a.row_elems = shape->num_kv_heads * shape->head_dim;
+    a.src_dtype = src_dtype;
+    a.cache_dtype = shape->cache_dtype;
+    {
+        volatile float one = 1.0f;
+        a.inv_scale = one / kv_scale_of(shape);  // rounded once, in fp32
+    }
+    hipError_t e = pa::launch_reshape_and_cache(a, (hipStream_t)stream);
+    return e == hipSuccess ? ok() : hip_fail(e, "reshape_and_cache launch");
+}
+
+size_t pa_decode_workspace_bytes(const pa_shape *shape)
+{
+    if (check_shape(shape, true) != PA_OK)
+        return 0;
+    return decode_layout(shape).total;
+}
+
+pa_status pa_decode(float *out, const void *q, const void *k_cache, const void *v_cache,
+                    const int32_t *block_tables, const int32_t *context_lens, float scale,
+                    const pa_shape *shape, void *workspace, size_t workspace_bytes, void *stream)
+{
+    pa_status st = check_shape(shape, true);
+    if (st != PA_OK)
+        return st;
+    const int G = shape->num_q_heads / shape->num_kv_heads;
+    if (shape->q_dtype != q_dtype_for(shape->cache_dtype))
+        return fail(PA_ERR_UNSUPPORTED, "q_dtype %d with cache_dtype %d", shape->q_dtype,
+                    shape->cache_dtype);
+    if (!pa::decode_supported(shape->cache_dtype, shape->head_dim, G))
+        return fail(PA_ERR_UNSUPPORTED, "decode not built for cache_dtype %d, head_dim %d, G %d",
+                    shape->cache_dtype, shape->head_dim, G);
+    if (shape->partition_tokens < 0 || shape->partition_tokens % 16 != 0)
+        return fail(PA_ERR_INVALID, "partition_tokens must be 0 or a positive multiple of 16");
+    if (!std::isfinite(scale))
+        return fail(PA_ERR_INVALID, "scale is not finite");
+    if (shape->num_seqs == 0)
+        return ok();
+    if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
+        return fail(PA_ERR_INVALID, "NULL data pointer");
+    const DecodeLayout L = decode_layout(shape);
+    if (!workspace || workspace_bytes < L.total)
+        return fail(PA_ERR_WORKSPACE, "decode needs %zu workspace bytes, got %zu", L.total,
+                    workspace ? workspace_bytes : (size_t)0);
+    pa::DecodeArgs a;
+    a.out = out;
+    a.q = q;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.block_tables = block_tables;
+    a.context_lens = context_lens;
+    a.num_seqs = shape->num_seqs;
+    a.num_q_heads = shape->num_q_heads;
+    a.num_kv_heads = shape->num_kv_heads;
+    a.head_dim = shape->head_dim;
+    a.max_blocks = shape->max_blocks_per_seq;
+    a.num_blocks = shape->num_blocks;
+    a.cache_dtype = shape->cache_dtype;
+    a.part_blocks = shape->partition_tokens / 16;
+    a.grid = decode_grid();
+    const float kvs = kv_scale_of(shape);
+    a.qk_scale = scale * 1.4426950408889634f * kvs;
+    a.v_scale = kvs;
+    char *ws = (char *)workspace;
+    a.ws_acc = (float *)ws;
+    a.ws_ml = (float *)(ws + L.acc_bytes);
+    a.ws_lohi = (int32_t *)(ws + L.acc_bytes + L.ml_bytes);
+    hipError_t e = pa::launch_decode(a, (hipStream_t)stream);
+    return e == hipSuccess ? ok() : hip_fail(e, "decode launch");
+}
+
+size_t pa_prefill_workspace_bytes(const pa_shape *shape, int64_t total_query_rows)
+{
+    if (check_shape(shape, true) != PA_OK || total_query_rows < 0)
+        return 0;
+    const int ks = pa::prefill_kv_splits(total_query_rows, shape->num_q_heads);
+    if (ks <= 1)
+        return 0;
+    const size_t rows = (size_t)total_query_rows * shape->num_q_heads;
+    return align256((size_t)ks * rows * shape->head_dim * sizeof(float)) +
+           align256((size_t)ks * rows * 2 * sizeof(float));
+}
+
+pa_status pa_prefill_chunk(float *out, const void *q, const void *k_cache, const void *v_cache,
+                           const int32_t *block_tables, const int32_t *query_start,
+                           const int32_t *context_lens, int64_t total_query_rows, float scale,
+                           const pa_shape *shape, void *workspace, size_t workspace_bytes,
+                           void *stream)
+{
+    pa_status st = check_shape(shape, true);
+    if (st != PA_OK)
+        return st;
+    const int G = shape->num_q_heads / shape->num_kv_heads;
+    if (shape->q_dtype != PA_BF16)
+        return fail(PA_ERR_UNSUPPORTED, "prefill needs a bf16 q");
+    if (!pa::prefill_supported(shape->cache_dtype, shape->head_dim, G))
+        return fail(PA_ERR_UNSUPPORTED, "prefill not built for cache_dtype %d, head_dim %d, G %d",
+                    shape->cache_dtype, shape->head_dim, G);
+    if (total_query_rows < 0)
+        return fail(PA_ERR_INVALID, "total_query_rows < 0");
+    if (total_query_rows > (int64_t)1 << 24)
+        return fail(PA_ERR_UNSUPPORTED, "more than 2^24 query rows");
+    if (!std::isfinite(scale))
+        return fail(PA_ERR_INVALID, "scale is not finite");
+    if (shape->num_seqs == 0 || total_query_rows == 0)
+        return ok();
+    if (!out || !q || !k_cache || !v_cache || !block_tables || !query_start || !context_lens)
+        return fail(PA_ERR_INVALID, "NULL data pointer");
+    const size_t need = pa_prefill_workspace_bytes(shape, total_query_rows);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return fail(PA_ERR_WORKSPACE, "prefill needs %zu workspace bytes, got %zu", need,
+                    workspace ? workspace_bytes : (size_t)0);
+    pa::PrefillArgs a;
+    a.out = out;
+    a.q = q;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.block_tables = block_tables;
+    a.query_start = query_start;
+    a.context_lens = context_lens;
+    a.total_rows = total_query_rows;
+    a.num_reqs = shape->num_seqs;
+    a.num_q_heads = shape->num_q_heads;
+    a.num_kv_heads = shape->num_kv_heads;
+    a.head_dim = shape->head_dim;
+    a.max_blocks = shape->max_blocks_per_seq;
+    a.num_blocks = shape->num_blocks;
+    a.cache_dtype = shape->cache_dtype;
+    a.kv_splits = pa::prefill_kv_splits(total_query_rows, shape->num_q_heads);
+    const float kvs = kv_scale_of(shape);
+    a.qk_scale = scale * 1.4426950408889634f * kvs;
+    a.v_scale = kvs;
+    const size_t rows = (size_t)total_query_rows * shape->num_q_heads;
+    a.ws_acc = (float *)workspace;
+    a.ws_ml = need > 0 ? (float *)((char *)workspace +
+                                   align256((size_t)a.kv_splits * rows * shape->head_dim * 4))
+                       : nullptr;
+    hipError_t e = pa::launch_prefill(a, (hipStream_t)stream);
+    return e == hipSuccess ? ok() : hip_fail(e, "prefill launch");
+}
+
+}  // extern "C"

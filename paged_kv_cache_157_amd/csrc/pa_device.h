@@ -1,0 +1,82 @@
+// pa_device.h -- device-side building blocks shared by the HIP kernels of
+// libpa (gfx950 / CDNA4, wave64).  Product code: nothing here is used by, or
+// uses, the CPU oracle.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+// Storage types (same numbering as pa_dtype in include/pa.h).
+enum : int { DT_F32 = 0, DT_BF16 = 1, DT_FP8 = 2 };
+
+template <int DT>
+struct Storage {
+    static constexpr int bytes = DT == DT_F32 ? 4 : DT == DT_BF16 ? 2 : 1;
+    static constexpr int per16 = 16 / bytes;  // elements in one 16-byte chunk
+};
+
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+
+static constexpr float kLog2e = 1.4426950408889634f;
+
+// bf16 halves of a packed dword, widened to fp32 exactly.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ __forceinline__ bf16x2 as_bf16x2(uint32_t w) { return __builtin_bit_cast(bf16x2, w); }
+
+// v_dot2_f32_bf16: a.lo*b.lo + a.hi*b.hi + c, fp32 accumulate.
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c)
+{
+    return __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(a), as_bf16x2(b), c, false);
+}
+
+// Two OCP E4M3 bytes (low or high half of a dword) -> two bf16, exactly.
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w)
+{
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+}
+
+// Two OCP E4M3 bytes -> two fp32, exactly.
+template <bool HI>
+__device__ __forceinline__ f32x2 fp8x2_to_f32x2(uint32_t w)
+{
+    return __builtin_amdgcn_cvt_pk_f32_fp8((int)w, HI);
+}
+
+// ---------------------------------------------------------------------------
+// DPP lane exchange inside 16-lane rows (all row/bank masks enabled).
+// ---------------------------------------------------------------------------
+enum : int {
+    DPP_QP_X1 = 0xB1,        // quad_perm [1,0,3,2]: partner lane ^ 1
+    DPP_QP_X2 = 0x4E,        // quad_perm [2,3,0,1]: partner lane ^ 2
+    DPP_ROW_ROR4 = 0x124,    // lane (l + 4) mod 16 within the row
+    DPP_ROW_ROR8 = 0x128,    // lane (l + 8) mod 16 = l ^ 8 within the row
+    DPP_HALF_MIRROR = 0x141, // lane l ^ 7 within each half row
+};
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x)
+{
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
+}
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+template <typename T>
+__device__ __forceinline__ T uniform(T v)
+{
+    return __builtin_bit_cast(T, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));
+}
+
+__device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+}  // namespace pa

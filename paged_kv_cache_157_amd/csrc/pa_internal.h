@@ -1,0 +1,63 @@
+// pa_internal.h -- host-side interface between the C ABI layer (pa_api.cpp)
+// and the kernel launchers (*.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pa {
+
+struct ReshapeArgs {
+    const void *k, *v;
+    void *k_cache, *v_cache;
+    const int64_t *slot_mapping;
+    int64_t num_tokens;
+    int64_t num_slots;   // num_blocks * 16
+    int row_elems;       // num_kv_heads * head_dim
+    int src_dtype, cache_dtype;
+    float inv_scale;     // fp32 reciprocal of kv_scale, rounded on the host
+};
+hipError_t launch_reshape_and_cache(const ReshapeArgs &a, hipStream_t stream);
+
+struct DecodeArgs {
+    float *out;
+    const void *q;
+    const void *k_cache, *v_cache;
+    const int32_t *block_tables, *context_lens;
+    int num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks;
+    int64_t num_blocks;
+    int cache_dtype;
+    int part_blocks;       // 0: balanced split; else fixed partitions (blocks)
+    int grid;              // persistent work-group count
+    float qk_scale;        // softmax scale * log2(e) (* kv_scale for fp8 K)
+    float v_scale;         // 1, or kv_scale for fp8 V
+    float *ws_acc;         // [slots][G][D]
+    float *ws_ml;          // [slots][G][2]
+    int32_t *ws_lohi;      // [S * Hkv][2]
+};
+// Number of partial-result slots the decode workspace must hold.
+int64_t decode_partial_slots(int num_seqs, int num_kv_heads, int max_blocks, int part_blocks,
+                             int grid);
+bool decode_supported(int cache_dtype, int head_dim, int group);
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
+
+struct PrefillArgs {
+    float *out;
+    const void *q;
+    const void *k_cache, *v_cache;
+    const int32_t *block_tables, *query_start, *context_lens;
+    int64_t total_rows;
+    int num_reqs, num_q_heads, num_kv_heads, head_dim, max_blocks;
+    int64_t num_blocks;
+    int cache_dtype;
+    int kv_splits;
+    float qk_scale, v_scale;
+    float *ws_acc;         // [kv_splits][rows*Hq][D]
+    float *ws_ml;          // [kv_splits][rows*Hq][2]
+};
+bool prefill_supported(int cache_dtype, int head_dim, int group);
+int prefill_kv_splits(int64_t total_rows, int num_q_heads);
+hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);
+
+}  // namespace pa

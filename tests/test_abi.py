@@ -1,0 +1,125 @@
+"""The C ABI library loads, exports what include/pa.h declares, and rejects
+bad arguments on the host before any launch (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from paged_kv_cache_157_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    names = []
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", fn)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names += re.findall(r"\b(pa_[a-z0-9_]+)\s*\(", text)
+    return sorted(set(names))
+
+
+def test_every_declared_symbol_is_exported():
+    lib = binding.load()
+    names = declared_functions()
+    assert len(names) >= 7
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in include/ but not exported"
+
+
+def test_struct_layout_matches_header():
+    assert ctypes.sizeof(binding.PAShape) == 48
+    assert binding.PAShape.num_blocks.offset == 16
+    assert binding.PAShape.partition_tokens.offset == 40
+
+
+def _shape(**kw):
+    base = dict(num_seqs=2, num_q_heads=8, num_kv_heads=2, head_dim=128, num_blocks=10,
+                max_blocks_per_seq=4, q_dtype=1, cache_dtype=1, kv_scale=1.0,
+                partition_tokens=0)
+    base.update(kw)
+    return binding.PAShape(**base)
+
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation
+
+
+def decode(shape, ws=FAKE, ws_bytes=1 << 40, ptr=FAKE, scale=0.1):
+    lib = binding.load()
+    return lib.pa_decode(ptr, ptr, ptr, ptr, ptr, ptr, scale, ctypes.byref(shape), ws, ws_bytes,
+                         None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(num_q_heads=7, num_kv_heads=2), binding.PA_ERR_INVALID),
+    (dict(num_q_heads=0), binding.PA_ERR_INVALID),
+    (dict(num_seqs=-1), binding.PA_ERR_INVALID),
+    (dict(head_dim=96), binding.PA_ERR_UNSUPPORTED),
+    (dict(num_q_heads=18, num_kv_heads=2), binding.PA_ERR_UNSUPPORTED),
+    (dict(num_blocks=0), binding.PA_ERR_INVALID),
+    (dict(max_blocks_per_seq=0), binding.PA_ERR_INVALID),
+    (dict(cache_dtype=7), binding.PA_ERR_INVALID),
+    (dict(cache_dtype=2, kv_scale=0.0), binding.PA_ERR_INVALID),
+    (dict(cache_dtype=0, q_dtype=0, head_dim=128), binding.PA_ERR_UNSUPPORTED),
+    (dict(q_dtype=0), binding.PA_ERR_UNSUPPORTED),
+    (dict(partition_tokens=24), binding.PA_ERR_INVALID),
+])
+def test_decode_rejects_bad_shapes(kw, status):
+    assert decode(_shape(**kw)) == status
+    assert binding.load().pa_last_error().decode() != ""
+
+
+def test_decode_rejects_null_pointers_and_small_workspace():
+    lib = binding.load()
+    assert decode(_shape(), ptr=None) == binding.PA_ERR_INVALID
+    assert decode(_shape(), ws=None) == binding.PA_ERR_WORKSPACE
+    assert decode(_shape(), ws_bytes=16) == binding.PA_ERR_WORKSPACE
+    assert decode(_shape(), scale=float("nan")) == binding.PA_ERR_INVALID
+    assert lib.pa_decode_workspace_bytes(ctypes.byref(_shape())) > 0
+    assert lib.pa_decode_workspace_bytes(ctypes.byref(_shape(head_dim=96))) == 0
+
+
+def test_decode_with_no_sequences_is_a_noop():
+    assert decode(_shape(num_seqs=0), ptr=None, ws=None) == binding.PA_OK
+
+
+def test_reshape_rejects_bad_arguments():
+    lib = binding.load()
+    s = _shape()
+    P = FAKE
+    assert lib.pa_reshape_and_cache(P, P, P, P, P, -1, 1, ctypes.byref(s), None) == \
+        binding.PA_ERR_INVALID
+    assert lib.pa_reshape_and_cache(P, P, P, P, P, 4, 0, ctypes.byref(s), None) == \
+        binding.PA_ERR_UNSUPPORTED
+    assert lib.pa_reshape_and_cache(None, P, P, P, P, 4, 1, ctypes.byref(s), None) == \
+        binding.PA_ERR_INVALID
+    assert lib.pa_reshape_and_cache(None, None, None, None, None, 0, 1, ctypes.byref(s),
+                                    None) == binding.PA_OK
+    assert lib.pa_reshape_and_cache(P, P, P, P, P, 4, 1, None, None) == binding.PA_ERR_INVALID
+
+
+def test_prefill_rejects_bad_arguments():
+    lib = binding.load()
+    P = FAKE
+    s = _shape(num_seqs=1)
+    assert lib.pa_prefill_chunk(P, P, P, P, P, P, P, -3, 0.1, ctypes.byref(s), P, 1 << 40,
+                                None) == binding.PA_ERR_INVALID
+    f32 = _shape(num_seqs=1, cache_dtype=0, q_dtype=0, head_dim=64)
+    assert lib.pa_prefill_chunk(P, P, P, P, P, P, P, 8, 0.1, ctypes.byref(f32), P, 1 << 40,
+                                None) == binding.PA_ERR_UNSUPPORTED
+    assert lib.pa_prefill_chunk(None, P, P, P, P, P, P, 8, 0.1, ctypes.byref(s), P, 1 << 40,
+                                None) == binding.PA_ERR_INVALID
+    big = lib.pa_prefill_workspace_bytes(ctypes.byref(_shape(num_seqs=1, num_q_heads=32,
+                                                             num_kv_heads=8)), 512)
+    assert big > 0
+    assert lib.pa_prefill_chunk(P, P, P, P, P, P, P, 512, 0.1,
+                                ctypes.byref(_shape(num_seqs=1, num_q_heads=32, num_kv_heads=8)),
+                                P, 16, None) == binding.PA_ERR_WORKSPACE
+
+
+def test_status_strings():
+    lib = binding.load()
+    for s in range(5):
+        assert lib.pa_status_string(s)
