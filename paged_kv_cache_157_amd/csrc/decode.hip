@@ -276,7 +276,11 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a)
             seg_items = (int)((long long)(n_i - x) < left ? (n_i - x) : left);
             b0 = x;
             b1 = x + seg_items;
-            slot = blockIdx.x + i * Hkv + g;
+            // rank of this work-group among those with a non-empty range: with at
+            // least as many items as work-groups every range is non-empty (rank =
+            // blockIdx.x); with fewer, each non-empty range holds one item (rank =
+            // a0).  Ranks keep the partial slots of one (sequence, head) contiguous.
+            slot = (int)(a0 < (long long)blockIdx.x ? a0 : (long long)blockIdx.x) + i * Hkv + g;
         }
         const bool first = x == 0;
         const bool last = x + seg_items == n_i;
@@ -443,9 +447,10 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a)
             }
 
             // -- probabilities to LDS --------------------------------------
+            const float m_use = my_mref == -INFINITY ? 0.f : my_mref;
 #pragma unroll
             for (int j = 0; j < ROUNDS; ++j) {
-                const float p = fast_exp2(sc[j] - my_mref);
+                const float p = fast_exp2(sc[j] - m_use);
                 if (lane_owner) {
                     lsum += p;
                     sm.p[w][row_token<LPT>(row, tr + j * C::TRN)][lane_m] = p;

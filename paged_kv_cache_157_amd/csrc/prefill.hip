@@ -244,6 +244,8 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a)
         // ---- probabilities and O += P V --------------------------------------------
         // P is split into a bf16 head and a bf16 tail (p = hi + lo to ~2^-16), so
         // the PV product keeps close to fp32 weights; both parts meet the same V.
+        // a row with no valid key yet keeps mref = -inf: its probabilities are 0
+        const float m_use = mref == -INFINITY ? 0.f : mref;
         u32x4 p_hi[4], p_lo[4];
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
@@ -251,7 +253,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a)
             float p[8], r[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                p[j] = fast_exp2(s[kc][base + j] - mref);
+                p[j] = fast_exp2(s[kc][base + j] - m_use);
                 lsum += p[j];
             }
             p_hi[ks] = u32x4{pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3]), pack_bf16(p[4], p[5]),
