@@ -12,7 +12,8 @@ HBM before the timed region.
 Prints one JSON line.  `value` is the effective KV bandwidth of the step: KV
 bytes the decode must read (each sequence's K and V rows, once) divided by
 the step time.  The roofline entry is for the decode launch (its two
-kernels), timed with HIP events on the stream the kernels run on.
+kernels), timed with HIP events on the stream the kernels run on, in a
+second pass right after the timed steps.
 """
 from __future__ import annotations
 
@@ -40,6 +41,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="qwen7b", choices=sorted(CONFIGS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="after timing, run one plain device copy of this many MiB "
+                         "(a known-size reference for hardware byte counters)")
     ap.add_argument("--traffic-json", default=os.path.join(os.path.dirname(__file__), "profiles",
                                                            "traffic.json"),
                     help="counter-measured HBM bytes per decode launch, if recorded")
@@ -119,50 +123,75 @@ def main():
     apply_cow(step)
     torch.cuda.synchronize()
 
-    def run_step(ev=None):
+    def cache_write():
         binding.reshape_and_cache(step.k_new, step.v_new, step.k_cache, step.v_cache,
                                   step.slot_mapping, kv_scale=cfg.kv_scale)
-        if out_pre is not None:
-            if ev is not None:
-                ev[2].record()
-            binding.prefill_chunk(out_pre, step.q_prefill, step.k_cache, step.v_cache,
-                                  step.prefill_table, step.prefill_query_start,
-                                  step.prefill_context, cfg.scale, kv_scale=cfg.kv_scale)
-            if ev is not None:
-                ev[3].record()
-        if ev is not None:
-            ev[0].record()
+
+    def prefill():
+        binding.prefill_chunk(out_pre, step.q_prefill, step.k_cache, step.v_cache,
+                              step.prefill_table, step.prefill_query_start, step.prefill_context,
+                              cfg.scale, kv_scale=cfg.kv_scale)
+
+    def decode():
         binding.decode(out, step.q, step.k_cache, step.v_cache, step.block_tables,
                        step.context_lens, cfg.scale, partition_tokens=cfg.partition_tokens,
                        kv_scale=cfg.kv_scale)
-        if ev is not None:
-            ev[1].record()
+
+    def run_step():
+        cache_write()
+        if out_pre is not None:
+            prefill()
+        decode()
 
     for _ in range(args.warmup):
         run_step()
     torch.cuda.synchronize()
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    # the timed region: K whole steps back to back (no events inside: an event
+    # record costs several microseconds of GPU idle time on this stack)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for k in range(args.steps):
-        run_step(events[k])
+    for _ in range(args.steps):
+        run_step()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
-    dec_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
-    pre_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in events])) if out_pre is not None \
-        else None
+
+    def launch_ms(fn, n):
+        """Average duration of one launch of fn: HIP events recorded on the stream
+        the kernels run on (torch's current stream) around n back-to-back launches
+        (one event pair, so the event cost is spread over n launches)."""
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        fn()
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    dec_ms = launch_ms(decode, args.steps)
+    pre_ms = launch_ms(prefill, args.steps) if out_pre is not None else None
+    cw_ms = launch_ms(cache_write, args.steps)
+    if args.copy_probe_mib:
+        # a plain device copy of known size: rocprofv3 --pmc reads of FETCH_SIZE /
+        # WRITE_SIZE for it convert the counters into bytes
+        n = args.copy_probe_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
 
     ab = algorithmic_bytes(cfg, step)
     kv_gbs = ab["kv"] / (ms_per_step * 1e-3) / 1e9
     achieved = ab["total"] / (dec_ms * 1e-3) / 1e9
     traffic = None
     if os.path.exists(args.traffic_json):
+        from paged_kv_cache_157_amd.rocprof_summary import decode_source_hash
         try:
             rec = json.load(open(args.traffic_json)).get(cfg.name)
-            if rec:
-                traffic = rec.get("bytes_per_launch")
+            if rec and rec.get("source_hash") == decode_source_hash():
+                traffic = rec.get("bytes_per_launch")  # counters of this very kernel
         except (OSError, ValueError):
             traffic = None
 
@@ -187,6 +216,7 @@ def main():
         "pct_of_hbm_peak": round(100.0 * kv_gbs / HBM_PEAK_GBS, 2),
         "tokens_per_s": round(cfg.num_seqs / (ms_per_step * 1e-3), 1),
         "decode_us": round(dec_ms * 1e3, 2),
+        "cache_write_us": round(cw_ms * 1e3, 2),
         "decode_kv_gbs": round(ab["kv"] / (dec_ms * 1e-3) / 1e9, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),

@@ -36,10 +36,11 @@ def common_flags():
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 
-def _compile(src: str, obj_dir: str) -> str:
+def _compile(src: str, obj_dir: str, defines=()) -> str:
     obj = os.path.join(obj_dir, os.path.basename(src) + ".o")
     lang = ["-x", "hip"] if src.endswith(".cpp") else []
-    cmd = [hipcc()] + common_flags() + ["-c"] + lang + [os.path.join(CSRC, src), "-o", obj]
+    cmd = ([hipcc()] + common_flags() + [f"-D{d}" for d in defines] + ["-c"] + lang +
+           [os.path.join(CSRC, src), "-o", obj])
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "not a recognized feature for this target"
     err = "\n".join(l for l in (r.stderr or "").splitlines() if noise not in l)
@@ -50,20 +51,22 @@ def _compile(src: str, obj_dir: str) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    obj_dir = os.path.join(HERE, "_build")
+def build(verbose: bool = True, defines=(), out: str = LIB) -> str:
+    """Compile every source and link `out` (default: the in-tree libpa.so).
+    `defines` are extra -D switches (tuning constants such as DECODE_STAGES)."""
+    obj_dir = os.path.join(HERE, "_build" if not defines else "_build_" + "_".join(defines))
     os.makedirs(obj_dir, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, obj_dir), SOURCES))
-    tmp = LIB + ".tmp%d" % os.getpid()
+        objs = list(ex.map(lambda s: _compile(s, obj_dir, defines), SOURCES))
+    tmp = out + ".tmp%d" % os.getpid()
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link of libpa.so failed:\n" + r.stderr)
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {out}")
+    return out
 
 
 if __name__ == "__main__":

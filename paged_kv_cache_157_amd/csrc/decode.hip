@@ -37,6 +37,10 @@
 
 namespace pa {
 
+#ifndef DECODE_STAGES
+#define DECODE_STAGES 2  // blocks of K/V in a wave's LDS ring (NSTAGE - 1 in flight)
+#endif
+
 template <int CDT, int D, int G>
 struct DecodeCfg {
     static constexpr int EB = Storage<CDT>::bytes;
@@ -132,37 +136,65 @@ __device__ __forceinline__ float sum_rows(float v)
     return v;
 }
 
-struct SegInfo {
-    int i, g;
-    int b0, b1;      // block range
-    int slot;
-    int first, last;
-};
-
-template <int CDT, int D, int G>
+template <int CDT, int D, int G, int NSTAGE>
 struct DecodeSmem {
     using C = DecodeCfg<CDT, D, G>;
+    static constexpr int KB = 16 * D * C::EB;  // bytes of one block of one KV head (K or V)
+    union {
+        // per-wave ring of NSTAGE blocks, K then V, filled by global->LDS DMA
+        uint8_t ring[C::WAVES][NSTAGE][2 * KB];
+        float acc[C::WAVES][G][D];  // per-wave accumulators at a segment end
+    };
     float p[C::WAVES][16][8];       // probabilities of the current block
     float bmax[C::WAVES][4][8];     // row maxima (rescale path)
-    float acc[C::WAVES][G][D];      // per-wave accumulators at a segment end
     float msum[C::WAVES][2][8];     // per-wave running max and sum
     long long scan[256];
-    int seg_i, seg_x;
+    int seg_i;
     long long seg_base;
 };
 
-template <int CDT, int D, int G>
+// s_waitcnt vmcnt(N): the global->LDS loads of the ring are counted there and
+// the compiler does not wait for them by itself.
+template <int N>
+__device__ __forceinline__ void wait_vm()
+{
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+template <int LPB, int NSTAGE>
+__device__ __forceinline__ void wait_blocks_after(int n)
+{
+    // n = blocks whose loads were issued after the one about to be read
+    if constexpr (NSTAGE >= 4) {
+        if (n >= 3) { wait_vm<3 * LPB>(); return; }
+    }
+    if constexpr (NSTAGE >= 3) {
+        if (n >= 2) { wait_vm<2 * LPB>(); return; }
+    }
+    if (n >= 1) { wait_vm<LPB>(); return; }
+    wait_vm<0>();
+}
+
+__device__ __forceinline__ void dma16(const void *src, void *lds_dst)
+{
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)lds_dst, 16, 0, 0);
+}
+
+template <int CDT, int D, int G, int NSTAGE>
 __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a)
 {
     using C = DecodeCfg<CDT, D, G>;
+    using SM = DecodeSmem<CDT, D, G, NSTAGE>;
     constexpr int LPT = C::LPT, GP = C::GP, CPL = C::CPL, ROUNDS = C::ROUNDS;
     constexpr int NC = C::NC, E = C::E, VTPR = C::VTPR, VPASS = C::VPASS, QW = C::QW;
+    constexpr int KB = SM::KB;
+    constexpr int LPB = 2 * KB / 1024;  // DMA instructions per block (K and V)
+    static_assert(ROUNDS * CPL * 1024 == KB && VPASS * 1024 == KB, "DMA layout");
     constexpr float TAU = 8.0f;
-    __shared__ DecodeSmem<CDT, D, G> sm;
+    __shared__ SM sm;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int w = tid >> 6;
+    const int w = uniform(tid >> 6);
     const int S = a.num_seqs, Hkv = a.num_kv_heads, Hq = a.num_q_heads, maxB = a.max_blocks;
     const int PB = a.part_blocks;
 
@@ -184,7 +216,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a)
             sm.scan[tid] += sm.scan[tid + s];
         __syncthreads();
     }
-    const long long total = sm.scan[0] * Hkv;
+    const long long total = uniform64(sm.scan[0]) * Hkv;
     __syncthreads();
     const long long a0 = total * blockIdx.x / gridDim.x;
     const long long a1 = total * (blockIdx.x + 1) / gridDim.x;
@@ -221,7 +253,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a)
     int i = uniform(sm.seg_i);
     if (i < 0)  // unreachable while a0 < total; keeps every index in range
         return;
-    long long base_i = sm.seg_base;  // first item index of sequence i
+    long long base_i = uniform64(sm.seg_base);  // first item index of sequence i
     long long item = a0;
     const int lane_m = head_mask<LPT, GP>(lane);
     const bool lane_owner = mask_owner<LPT, GP>(lane) && lane_m < G;
@@ -236,9 +268,11 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a)
 
     const int64_t tok_bytes = (int64_t)Hkv * D * C::EB;
     const int64_t blk_bytes = 16 * tok_bytes;
-    const int64_t nslots = a.num_blocks;
+    const unsigned nblocks_pool = (unsigned)a.num_blocks;
 
-    // per-lane byte offsets of K and V chunks inside one block (KV head 0)
+    // per-lane byte offsets of the K and V chunks this lane fetches inside one
+    // block (KV head 0); the DMA puts chunk (j, c) of lane l at LDS
+    // (j*CPL + c)*1024 + 16*l, so every lane reads back exactly what it fetched
     int koff[ROUNDS][CPL];
 #pragma unroll
     for (int j = 0; j < ROUNDS; ++j)
@@ -251,19 +285,23 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a)
     for (int v = 0; v < VPASS; ++v)
         voff[v] = (int)(row_token<LPT>(row, v * VTPR + vh) * tok_bytes) + vc * 16;
 
+    uint8_t *my_ring = &sm.ring[w][0][0];
+
+    const auto lens_s = scalar_view(a.context_lens);
     while (item < a1) {
-        // ---- next segment ------------------------------------------------
-        int L = a.context_lens[i];
+        // ---- next segment (every value here is wave-uniform) ---------------
+        int L = lens_s[i];
         int n_i = items_of(L);
         while (n_i == 0) {  // cannot happen for the first segment; skip empties
             ++i;
-            L = a.context_lens[i];
+            L = lens_s[i];
             n_i = items_of(L);
         }
-        L = L > maxB * 16 ? maxB * 16 : L;
+        L = uniform(L > maxB * 16 ? maxB * 16 : L);
+        n_i = uniform(n_i);
         const long long rel = item - base_i;
-        const int g = (int)(rel / n_i);
-        const int x = (int)(rel - (long long)g * n_i);
+        const int g = uniform((int)(rel / n_i));
+        const int x = uniform((int)(rel - (long long)g * n_i));
         const int nblk = (L + 15) >> 4;
         int seg_items, b0, b1, slot;
         if (PB > 0) {
@@ -282,11 +320,13 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a)
             // a0).  Ranks keep the partial slots of one (sequence, head) contiguous.
             slot = (int)(a0 < (long long)blockIdx.x ? a0 : (long long)blockIdx.x) + i * Hkv + g;
         }
+        b0 = uniform(b0);
+        b1 = uniform(b1);
         const bool first = x == 0;
         const bool last = x + seg_items == n_i;
         const bool direct = first && last;
 
-        // ---- load q for this (sequence, KV head) --------------------------
+        // ---- q for this (sequence, KV head), slot s = head (s ^ lane_m) ---
         uint32_t qr[GP][CPL][QW];
         {
             const int hq0 = g * G;
@@ -322,6 +362,14 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a)
                     }
                 }
             }
+            // q must land before the ring's DMA loads are queued behind it
+#pragma unroll
+            for (int s = 0; s < GP; ++s)
+#pragma unroll
+                for (int c = 0; c < CPL; ++c)
+#pragma unroll
+                    for (int k = 0; k < QW; ++k)
+                        settle(qr[s][c][k]);
         }
 
         // ---- per-wave streaming softmax over blocks b0+w, b0+w+4, ... -----
@@ -338,34 +386,44 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a)
         float my_mref = -INFINITY;
         float lsum = 0.f;
 
-        const int32_t *table = a.block_tables + (int64_t)i * maxB;
+        const auto table = scalar_view(a.block_tables + (int64_t)i * maxB);
         const char *kbase = (const char *)a.k_cache + (int64_t)g * D * C::EB;
         const char *vbase = (const char *)a.v_cache + (int64_t)g * D * C::EB;
 
-        u32x4 kb[ROUNDS][CPL], vb[VPASS];
-        auto load_block = [&](int b, u32x4 (&kd)[ROUNDS][CPL], u32x4 (&vd)[VPASS]) {
-            int pb = table[b];
-            pb = (unsigned)pb < (unsigned)nslots ? pb : 0;
+        // blocks of this wave: b0 + w + 4t, t < nb_w
+        const int nb_w = b1 - b0 - w > 0 ? (b1 - b0 - w + C::WAVES - 1) / C::WAVES : 0;
+        auto issue = [&](int t, int pb) {
+            pb = (unsigned)pb < nblocks_pool ? pb : 0;
             const char *kp = kbase + (int64_t)pb * blk_bytes;
             const char *vp = vbase + (int64_t)pb * blk_bytes;
+            uint8_t *st = my_ring + (t % NSTAGE) * 2 * KB;
 #pragma unroll
             for (int j = 0; j < ROUNDS; ++j)
 #pragma unroll
                 for (int c = 0; c < CPL; ++c)
-                    kd[j][c] = *(const u32x4 *)(kp + koff[j][c]);
+                    dma16(kp + koff[j][c], st + (j * CPL + c) * 1024);
 #pragma unroll
             for (int v = 0; v < VPASS; ++v)
-                vd[v] = *(const u32x4 *)(vp + voff[v]);
+                dma16(vp + voff[v], st + KB + v * 1024);
         };
+        // prologue: NSTAGE - 1 blocks in flight
+#pragma unroll
+        for (int t = 0; t < NSTAGE - 1; ++t)
+            if (t < nb_w)
+                issue(t, uniform(table[b0 + w + 4 * t]));
+        int pb_ahead = NSTAGE - 1 < nb_w ? uniform(table[b0 + w + 4 * (NSTAGE - 1)]) : 0;
 
-        int b = b0 + w;
-        if (b < b1)
-            load_block(b, kb, vb);
-        for (; b < b1; b += C::WAVES) {
-            u32x4 kn[ROUNDS][CPL], vn[VPASS];
-            const bool has_next = b + C::WAVES < b1;
-            if (has_next)
-                load_block(b + C::WAVES, kn, vn);
+        for (int t = 0; t < nb_w; ++t) {
+            const int b = b0 + w + 4 * t;
+            // keep NSTAGE - 1 blocks ahead in flight; fetch the next table entry early
+            if (t + NSTAGE - 1 < nb_w) {
+                issue(t + NSTAGE - 1, pb_ahead);
+                if (t + NSTAGE < nb_w)
+                    pb_ahead = uniform(table[b + 4 * NSTAGE]);
+            }
+            const int after = nb_w - 1 - t < NSTAGE - 1 ? nb_w - 1 - t : NSTAGE - 1;
+            wait_blocks_after<LPB, NSTAGE>(after);
+            const uint8_t *st = my_ring + (t % NSTAGE) * 2 * KB + lane * 16;
 
             // -- scores of this lane's token(s) for head lane_m ------------
             const int tbase = b * 16;
@@ -378,18 +436,19 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a)
                     xs[s] = 0.f;
 #pragma unroll
                 for (int c = 0; c < CPL; ++c) {
+                    const u32x4 kc = *(const u32x4 *)(st + (j * CPL + c) * 1024);
                     if constexpr (CDT == DT_BF16) {
 #pragma unroll
                         for (int s = 0; s < GP; ++s)
 #pragma unroll
                             for (int p = 0; p < 4; ++p)
-                                xs[s] = dot2_bf16(qr[s][c][p], kb[j][c][p], xs[s]);
+                                xs[s] = dot2_bf16(qr[s][c][p], kc[p], xs[s]);
                     } else if constexpr (CDT == DT_FP8) {
                         uint32_t kk[8];
 #pragma unroll
                         for (int p = 0; p < 4; ++p) {
-                            kk[2 * p] = fp8x2_to_bf16x2<false>(kb[j][c][p]);
-                            kk[2 * p + 1] = fp8x2_to_bf16x2<true>(kb[j][c][p]);
+                            kk[2 * p] = fp8x2_to_bf16x2<false>(kc[p]);
+                            kk[2 * p + 1] = fp8x2_to_bf16x2<true>(kc[p]);
                         }
 #pragma unroll
                         for (int s = 0; s < GP; ++s)
@@ -401,13 +460,13 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a)
                         for (int s = 0; s < GP; ++s)
 #pragma unroll
                             for (int p = 0; p < 4; ++p)
-                                xs[s] = fmaf(__uint_as_float(qr[s][c][p]),
-                                             __uint_as_float(kb[j][c][p]), xs[s]);
+                                xs[s] = fmaf(__uint_as_float(qr[s][c][p]), __uint_as_float(kc[p]),
+                                             xs[s]);
                     }
                 }
                 const float s2 = reduce_scatter<LPT, GP>(xs) * a.qk_scale;
-                const int t = tbase + row_token<LPT>(row, tr + j * C::TRN);
-                sc[j] = t < L ? s2 : -INFINITY;
+                const int tt = tbase + row_token<LPT>(row, tr + j * C::TRN);
+                sc[j] = tt < L ? s2 : -INFINITY;
             }
 
             // -- block maximum of the row for head lane_m ------------------
@@ -423,8 +482,8 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a)
                 // raise the wave's reference maximum for every head
                 if (lane_owner && tr == 0)
                     sm.bmax[w][row][lane_m] = bm;
-                __builtin_amdgcn_wave_barrier();
                 __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+                __builtin_amdgcn_wave_barrier();
                 float my_alpha = 1.f;
 #pragma unroll
                 for (int h = 0; h < G; ++h) {
@@ -464,7 +523,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a)
 #pragma unroll
             for (int v = 0; v < VPASS; ++v) {
                 const int tk = row_token<LPT>(row, v * VTPR + vh);
-                u32x4 vv = vb[v];
+                u32x4 vv = *(const u32x4 *)(st + KB + v * 1024);
                 if (partial && tbase + tk >= L)
                     vv = u32x4{0u, 0u, 0u, 0u};
                 float pr[G];
@@ -501,17 +560,6 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a)
             }
             __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
             __builtin_amdgcn_wave_barrier();
-
-            if (has_next) {
-#pragma unroll
-                for (int j = 0; j < ROUNDS; ++j)
-#pragma unroll
-                    for (int c = 0; c < CPL; ++c)
-                        kb[j][c] = kn[j][c];
-#pragma unroll
-                for (int v = 0; v < VPASS; ++v)
-                    vb[v] = vn[v];
-            }
         }
 
         // ---- wave totals -> LDS --------------------------------------------
@@ -534,6 +582,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a)
                 }
                 acc[h][e] = t;
             }
+        __syncthreads();  // every wave is done with its ring (aliased below)
         if (lane < NC) {
 #pragma unroll
             for (int h = 0; h < G; ++h)
@@ -592,37 +641,45 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a)
     }
 }
 
-// Merge the partial results of every (sequence, KV head) that was split.
+// Merge the partial results of every (sequence, KV head) that was split:
+// out = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s, M = max_s m_s.
+// One work-group per (sequence, KV head), one thread per output element; the
+// slot loop is unrolled so its loads are in flight together.
 template <int D, int G>
-__global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeArgs a)
+__global__ __launch_bounds__(1024) void decode_reduce_kernel(DecodeArgs a)
 {
     const int Hkv = a.num_kv_heads, Hq = a.num_q_heads;
-    const int i = blockIdx.x / Hkv, g = blockIdx.x - (blockIdx.x / Hkv) * Hkv;
-    const int L = a.context_lens[i];
+    const int pair = blockIdx.x;
+    const int i = pair / Hkv, g = pair - (pair / Hkv) * Hkv;
+    const int e = threadIdx.x;
+    const int L = scalar_view(a.context_lens)[i];
     float *out = a.out + ((int64_t)i * Hq + g * G) * D;
+    if (e >= G * D)
+        return;
     if (L <= 0) {
-        for (int e = threadIdx.x; e < G * D; e += 256)
-            out[e] = 0.f;
+        out[e] = 0.f;
         return;
     }
-    const int lo = a.ws_lohi[((int64_t)i * Hkv + g) * 2 + 0];
-    const int hi = a.ws_lohi[((int64_t)i * Hkv + g) * 2 + 1];
+    const int lo = scalar_view(a.ws_lohi)[(int64_t)pair * 2 + 0];
+    const int hi = scalar_view(a.ws_lohi)[(int64_t)pair * 2 + 1];
     if (lo == hi)
         return;
-    for (int e = threadIdx.x; e < G * D; e += 256) {
-        const int h = e / D, c = e - h * D;
-        float M = -INFINITY;
-        for (int s = lo; s <= hi; ++s)
-            M = fmaxf(M, a.ws_ml[((int64_t)s * G + h) * 2]);
-        float num = 0.f, den = 0.f;
-        for (int s = lo; s <= hi; ++s) {
-            const float m = a.ws_ml[((int64_t)s * G + h) * 2];
-            const float f = m == -INFINITY ? 0.f : fast_exp2(m - M);
-            num += f * a.ws_acc[((int64_t)s * G + h) * D + c];
-            den += f * a.ws_ml[((int64_t)s * G + h) * 2 + 1];
-        }
-        out[e] = num / den * a.v_scale;
+    const int h = e / D;
+    const float *ml = a.ws_ml + ((int64_t)lo * G + h) * 2;
+    const float *acc = a.ws_acc + (int64_t)lo * G * D + e;
+    const int np = hi - lo + 1;
+    float M = -INFINITY;
+    for (int s = 0; s < np; ++s)
+        M = fmaxf(M, ml[(int64_t)s * G * 2]);
+    float num = 0.f, den = 0.f;
+#pragma unroll 4
+    for (int s = 0; s < np; ++s) {
+        const float m = ml[(int64_t)s * G * 2];
+        const float f = m == -INFINITY ? 0.f : fast_exp2(m - M);
+        num += f * acc[(int64_t)s * G * D];
+        den += f * ml[(int64_t)s * G * 2 + 1];
     }
+    out[e] = num / den * a.v_scale;
 }
 
 int64_t decode_partial_slots(int num_seqs, int num_kv_heads, int max_blocks, int part_blocks,
@@ -648,47 +705,56 @@ bool decode_supported(int cache_dtype, int head_dim, int group)
 }
 
 template <int CDT, int D, int G>
-static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t stream)
+static DecodeKernels kernels_t()
 {
-    decode_kernel<CDT, D, G><<<a.grid, 256, 0, stream>>>(a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess)
-        return e;
-    decode_reduce_kernel<D, G><<<a.num_seqs * a.num_kv_heads, 256, 0, stream>>>(a);
-    return hipGetLastError();
+    return DecodeKernels{(const void *)decode_kernel<CDT, D, G, DECODE_STAGES>,
+                         (const void *)decode_reduce_kernel<D, G>};
 }
 
 template <int CDT, int D>
-static hipError_t launch_decode_d(const DecodeArgs &a, hipStream_t stream)
+static DecodeKernels kernels_d(int G)
 {
-    switch (a.num_q_heads / a.num_kv_heads) {
-    case 1: return launch_decode_t<CDT, D, 1>(a, stream);
-    case 2: return launch_decode_t<CDT, D, 2>(a, stream);
-    case 3: return launch_decode_t<CDT, D, 3>(a, stream);
-    case 4: return launch_decode_t<CDT, D, 4>(a, stream);
-    case 5: return launch_decode_t<CDT, D, 5>(a, stream);
-    case 6: return launch_decode_t<CDT, D, 6>(a, stream);
-    case 7: return launch_decode_t<CDT, D, 7>(a, stream);
-    default: return launch_decode_t<CDT, D, 8>(a, stream);
+    switch (G) {
+    case 1: return kernels_t<CDT, D, 1>();
+    case 2: return kernels_t<CDT, D, 2>();
+    case 3: return kernels_t<CDT, D, 3>();
+    case 4: return kernels_t<CDT, D, 4>();
+    case 5: return kernels_t<CDT, D, 5>();
+    case 6: return kernels_t<CDT, D, 6>();
+    case 7: return kernels_t<CDT, D, 7>();
+    default: return kernels_t<CDT, D, 8>();
     }
+}
+
+DecodeKernels decode_kernels(int cache_dtype, int head_dim, int group)
+{
+    if (cache_dtype == DT_F32)
+        return kernels_d<DT_F32, 64>(group);
+    if (cache_dtype == DT_BF16)
+        return head_dim == 64 ? kernels_d<DT_BF16, 64>(group) : kernels_d<DT_BF16, 128>(group);
+    if (head_dim == 64) {
+        switch (group) {
+        case 1: return kernels_t<DT_FP8, 64, 1>();
+        case 2: return kernels_t<DT_FP8, 64, 2>();
+        case 3: return kernels_t<DT_FP8, 64, 3>();
+        default: return kernels_t<DT_FP8, 64, 4>();
+        }
+    }
+    return kernels_d<DT_FP8, 128>(group);
 }
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream)
 {
-    if (a.cache_dtype == DT_F32)
-        return launch_decode_d<DT_F32, 64>(a, stream);
-    if (a.cache_dtype == DT_BF16)
-        return a.head_dim == 64 ? launch_decode_d<DT_BF16, 64>(a, stream)
-                                : launch_decode_d<DT_BF16, 128>(a, stream);
-    if (a.head_dim == 64) {
-        switch (a.num_q_heads / a.num_kv_heads) {
-        case 1: return launch_decode_t<DT_FP8, 64, 1>(a, stream);
-        case 2: return launch_decode_t<DT_FP8, 64, 2>(a, stream);
-        case 3: return launch_decode_t<DT_FP8, 64, 3>(a, stream);
-        default: return launch_decode_t<DT_FP8, 64, 4>(a, stream);
-        }
-    }
-    return launch_decode_d<DT_FP8, 128>(a, stream);
+    const DecodeKernels k = decode_kernels(a.cache_dtype, a.head_dim, a.num_q_heads / a.num_kv_heads);
+    DecodeArgs args = a;
+    void *params[] = {&args};
+    hipError_t e = hipLaunchKernel(k.main, dim3(a.grid), dim3(256), params, 0, stream);
+    if (e != hipSuccess)
+        return e;
+    const int G = a.num_q_heads / a.num_kv_heads;
+    const unsigned threads = (unsigned)((G * a.head_dim + 63) / 64 * 64);
+    return hipLaunchKernel(k.reduce, dim3(a.num_seqs * a.num_kv_heads), dim3(threads), params, 0,
+                           stream);
 }
 
 }  // namespace pa

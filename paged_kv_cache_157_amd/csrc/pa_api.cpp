@@ -55,8 +55,30 @@ int device_cus()
     return cached[dev];
 }
 
-// Persistent decode grid: two work-groups per compute unit.
-int decode_grid() { return 2 * device_cus(); }
+// Persistent decode grid: as many work-groups as can be resident at once
+// (compute units x occupancy of the kernel that serves this shape), so every
+// work-group of the balanced split runs concurrently.
+int decode_grid(const pa_shape *s)
+{
+    static std::mutex mu;
+    static int cached[64][3][2][9] = {};
+    const int G = s->num_q_heads / s->num_kv_heads;
+    const int dt = s->cache_dtype, dh = s->head_dim == 128 ? 1 : 0;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return 256;
+    std::lock_guard<std::mutex> lock(mu);
+    int &slot = cached[dev][dt][dh][G];
+    if (slot == 0) {
+        int per_cu = 0;
+        const pa::DecodeKernels k = pa::decode_kernels(dt, s->head_dim, G);
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k.main, 256, 0) != hipSuccess ||
+            per_cu <= 0)
+            per_cu = 1;
+        slot = per_cu * device_cus();
+    }
+    return slot;
+}
 
 pa_status check_shape(const pa_shape *s, bool need_tables)
 {
@@ -101,7 +123,7 @@ DecodeLayout decode_layout(const pa_shape *s)
     const int pb = s->partition_tokens > 0 ? s->partition_tokens / 16 : 0;
     DecodeLayout L;
     L.slots = pa::decode_partial_slots(s->num_seqs, s->num_kv_heads, s->max_blocks_per_seq, pb,
-                                       decode_grid());
+                                       decode_grid(s));
     L.acc_bytes = align256((size_t)L.slots * G * s->head_dim * sizeof(float));
     L.ml_bytes = align256((size_t)L.slots * G * 2 * sizeof(float));
     L.lohi_bytes = align256((size_t)s->num_seqs * s->num_kv_heads * 2 * sizeof(int32_t));
@@ -166,6 +188,9 @@ size_t pa_decode_workspace_bytes(const pa_shape *shape)
 {
     if (check_shape(shape, true) != PA_OK)
         return 0;
+    if (!pa::decode_supported(shape->cache_dtype, shape->head_dim,
+                              shape->num_q_heads / shape->num_kv_heads))
+        return 0;
     return decode_layout(shape).total;
 }
 
@@ -210,7 +235,7 @@ pa_status pa_decode(float *out, const void *q, const void *k_cache, const void *
     a.num_blocks = shape->num_blocks;
     a.cache_dtype = shape->cache_dtype;
     a.part_blocks = shape->partition_tokens / 16;
-    a.grid = decode_grid();
+    a.grid = decode_grid(shape);
     const float kvs = kv_scale_of(shape);
     a.qk_scale = scale * 1.4426950408889634f * kvs;
     a.v_scale = kvs;

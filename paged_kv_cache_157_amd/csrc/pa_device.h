@@ -75,6 +75,25 @@ __device__ __forceinline__ T uniform(T v)
     return __builtin_bit_cast(T, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));
 }
 
+__device__ __forceinline__ long long uniform64(long long v)
+{
+    const uint64_t u = (uint64_t)v;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((int)(uint32_t)u);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((int)(uint32_t)(u >> 32));
+    return (long long)(((uint64_t)hi << 32) | lo);
+}
+
+// Read-only view of a global array through the constant address space: loads
+// at wave-uniform indices become scalar loads (counted by lgkmcnt, not vmcnt).
+template <typename T>
+__device__ __forceinline__ const __attribute__((address_space(4))) T *scalar_view(const T *p)
+{
+    return (const __attribute__((address_space(4))) T *)p;
+}
+
+// Make the compiler materialise a loaded value here (waiting for its load).
+__device__ __forceinline__ void settle(uint32_t v) { asm volatile("" ::"v"(v)); }
+
 __device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

@@ -40,6 +40,11 @@ struct DecodeArgs {
 int64_t decode_partial_slots(int num_seqs, int num_kv_heads, int max_blocks, int part_blocks,
                              int grid);
 bool decode_supported(int cache_dtype, int head_dim, int group);
+struct DecodeKernels {
+    const void *main;    // persistent split-K decode kernel
+    const void *reduce;  // partial-result merge
+};
+DecodeKernels decode_kernels(int cache_dtype, int head_dim, int group);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
 
 struct PrefillArgs {
