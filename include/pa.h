@@ -111,8 +111,15 @@ size_t pa_decode_workspace_bytes(const pa_shape *shape);
  *   context_lens:  [num_seqs] int32, tokens each query attends (its own
  *                  token included, written beforehand); 0 gives a zero row
  *   scale:         softmax scale (1/sqrt(head_dim) in the usual case)
- *   workspace:     device scratch of pa_decode_workspace_bytes(shape) bytes
- *                  (split-K partial results; contents need no initialisation)
+ *   workspace:     device scratch of pa_decode_workspace_bytes(shape) bytes:
+ *                  arrival counters (its first 4 MiB), then split-K partial
+ *                  results.  The counter region must be zero before the first
+ *                  call that uses the buffer; every call leaves it zero again,
+ *                  so a buffer zeroed once can be reused by calls of any shape.
+ *                  Calls that run concurrently need separate workspaces.
+ *   A call is one kernel launch: partial results of a sequence split across
+ *   work-groups are merged by the work-group that finishes last.
+ *   Requires num_seqs * num_kv_heads <= 2^20.
  */
 pa_status pa_decode(float *out, const void *q, const void *k_cache, const void *v_cache,
                     const int32_t *block_tables, const int32_t *context_lens, float scale,

@@ -125,7 +125,9 @@ def _workspace(device: torch.device, nbytes: int, op: str) -> Optional[torch.Ten
     key = (device.index if device.index is not None else torch.cuda.current_device(), op)
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        # zero-filled once: pa_decode's arrival counters must start at zero (every
+        # call leaves them zero again); nothing else in it needs initialisation
+        ws = torch.zeros(nbytes, dtype=torch.uint8, device=device)
         _workspaces[key] = ws
     return ws
 

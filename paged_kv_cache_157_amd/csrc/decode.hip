@@ -16,7 +16,9 @@
 //     batch of short ones.  A run of items of one (sequence, KV head) inside
 //     a range is a "segment".  A segment that covers its whole sequence
 //     writes the output directly; otherwise it writes a partial
-//     (max, sum, unnormalised accumulator) and a second kernel merges them.
+//     (max, sum, unnormalised accumulator); the work-group that delivers the
+//     last partial of a (sequence, KV head) merges them (arrival counter),
+//     so a call is a single kernel launch.
 //   * Inside a work-group the four waves take every fourth block of the
 //     segment.  A wave handles all G query heads of its KV head, so each
 //     K/V row fetched from HBM is used G times from registers.
@@ -40,6 +42,9 @@ namespace pa {
 #ifndef DECODE_STAGES
 #define DECODE_STAGES 2  // blocks of K/V in a wave's LDS ring (NSTAGE - 1 in flight)
 #endif
+#ifndef DECODE_WAVES
+#define DECODE_WAVES 4   // waves per work-group; they split a segment's blocks
+#endif
 
 template <int CDT, int D, int G>
 struct DecodeCfg {
@@ -55,7 +60,6 @@ struct DecodeCfg {
     static constexpr int VPASS = 4 / VTPR;       // V passes per block
     // q dwords per (head slot, K chunk): bf16 pairs matching the chunk, or fp32
     static constexpr int QW = CDT == DT_FP8 ? 8 : 4;
-    static constexpr int WAVES = 4;
     static_assert(CPL >= 1 && NC <= 16 && NC >= 4, "unsupported chunk geometry");
     static_assert(G >= 1 && G <= 8, "GQA group must be 1..8");
 };
@@ -136,19 +140,20 @@ __device__ __forceinline__ float sum_rows(float v)
     return v;
 }
 
-template <int CDT, int D, int G, int NSTAGE>
+template <int CDT, int D, int G, int NSTAGE, int WAVES>
 struct DecodeSmem {
     using C = DecodeCfg<CDT, D, G>;
     static constexpr int KB = 16 * D * C::EB;  // bytes of one block of one KV head (K or V)
     union {
         // per-wave ring of NSTAGE blocks, K then V, filled by global->LDS DMA
-        uint8_t ring[C::WAVES][NSTAGE][2 * KB];
-        float acc[C::WAVES][G][D];  // per-wave accumulators at a segment end
+        uint8_t ring[WAVES][NSTAGE][2 * KB];
+        float acc[WAVES][G][D];  // per-wave accumulators at a segment end
     };
-    float p[C::WAVES][16][8];       // probabilities of the current block
-    float bmax[C::WAVES][4][8];     // row maxima (rescale path)
-    float msum[C::WAVES][2][8];     // per-wave running max and sum
-    long long scan[256];
+    float p[WAVES][16][8];       // probabilities of the current block
+    float bmax[WAVES][4][8];     // row maxima (rescale path)
+    float msum[WAVES][2][8];     // per-wave running max and sum
+    long long scan[64 * WAVES];
+    int last;
     int seg_i;
     long long seg_base;
 };
@@ -179,11 +184,12 @@ __device__ __forceinline__ void dma16(const void *src, void *lds_dst)
     __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)lds_dst, 16, 0, 0);
 }
 
-template <int CDT, int D, int G, int NSTAGE>
-__global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a)
+template <int CDT, int D, int G, int NSTAGE, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void decode_kernel(DecodeArgs a)
 {
     using C = DecodeCfg<CDT, D, G>;
-    using SM = DecodeSmem<CDT, D, G, NSTAGE>;
+    using SM = DecodeSmem<CDT, D, G, NSTAGE, WAVES>;
+    constexpr int NT = 64 * WAVES;
     constexpr int LPT = C::LPT, GP = C::GP, CPL = C::CPL, ROUNDS = C::ROUNDS;
     constexpr int NC = C::NC, E = C::E, VTPR = C::VTPR, VPASS = C::VPASS, QW = C::QW;
     constexpr int KB = SM::KB;
@@ -207,17 +213,23 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a)
 
     // ---- total item count and this work-group's range --------------------
     long long part = 0;
-    for (int i = tid; i < S; i += 256)
+    for (int i = tid; i < S; i += NT)
         part += items_of(a.context_lens[i]);
     sm.scan[tid] = part;
     __syncthreads();
-    for (int s = 128; s > 0; s >>= 1) {
+    for (int s = NT / 2; s > 0; s >>= 1) {
         if (tid < s)
             sm.scan[tid] += sm.scan[tid + s];
         __syncthreads();
     }
     const long long total = uniform64(sm.scan[0]) * Hkv;
     __syncthreads();
+    if (blockIdx.x == 0) {  // sequences with no tokens get a zero output row
+        for (int i = tid; i < S; i += NT)
+            if (a.context_lens[i] <= 0)
+                for (int e = 0; e < Hq * D; ++e)
+                    a.out[(int64_t)i * Hq * D + e] = 0.f;
+    }
     const long long a0 = total * blockIdx.x / gridDim.x;
     const long long a1 = total * (blockIdx.x + 1) / gridDim.x;
     if (a0 >= a1)
@@ -227,13 +239,13 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a)
     if (tid == 0)
         sm.seg_i = -1;
     long long carry = 0;
-    for (int base = 0; base < S; base += 256) {
+    for (int base = 0; base < S; base += NT) {
         const int i = base + tid;
         const long long v = i < S ? (long long)items_of(a.context_lens[i]) * Hkv : 0;
         __syncthreads();
         sm.scan[tid] = v;
         __syncthreads();
-        for (int s = 1; s < 256; s <<= 1) {
+        for (int s = 1; s < NT; s <<= 1) {
             long long t = tid >= s ? sm.scan[tid - s] : 0;
             __syncthreads();
             sm.scan[tid] += t;
@@ -245,7 +257,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a)
             sm.seg_i = i;
             sm.seg_base = excl;
         }
-        carry += sm.scan[255];
+        carry += sm.scan[NT - 1];
         __syncthreads();
         if (sm.seg_i >= 0)
             break;
@@ -273,17 +285,17 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a)
     // per-lane byte offsets of the K and V chunks this lane fetches inside one
     // block (KV head 0); the DMA puts chunk (j, c) of lane l at LDS
     // (j*CPL + c)*1024 + 16*l, so every lane reads back exactly what it fetched
-    int koff[ROUNDS][CPL];
+    unsigned koff[ROUNDS][CPL];
 #pragma unroll
     for (int j = 0; j < ROUNDS; ++j)
 #pragma unroll
         for (int c = 0; c < CPL; ++c)
-            koff[j][c] = (int)(row_token<LPT>(row, tr + j * C::TRN) * tok_bytes) +
-                         (gl + c * LPT) * 16;
-    int voff[VPASS];
+            koff[j][c] = (unsigned)(row_token<LPT>(row, tr + j * C::TRN) * tok_bytes) +
+                         (unsigned)((gl + c * LPT) * 16);
+    unsigned voff[VPASS];
 #pragma unroll
     for (int v = 0; v < VPASS; ++v)
-        voff[v] = (int)(row_token<LPT>(row, v * VTPR + vh) * tok_bytes) + vc * 16;
+        voff[v] = (unsigned)(row_token<LPT>(row, v * VTPR + vh) * tok_bytes) + (unsigned)(vc * 16);
 
     uint8_t *my_ring = &sm.ring[w][0][0];
 
@@ -372,7 +384,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a)
                         settle(qr[s][c][k]);
         }
 
-        // ---- per-wave streaming softmax over blocks b0+w, b0+w+4, ... -----
+        // ---- per-wave streaming softmax over blocks b0+w, b0+w+WAVES, ... ---
         float acc[G][E];
 #pragma unroll
         for (int h = 0; h < G; ++h)
@@ -390,8 +402,8 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a)
         const char *kbase = (const char *)a.k_cache + (int64_t)g * D * C::EB;
         const char *vbase = (const char *)a.v_cache + (int64_t)g * D * C::EB;
 
-        // blocks of this wave: b0 + w + 4t, t < nb_w
-        const int nb_w = b1 - b0 - w > 0 ? (b1 - b0 - w + C::WAVES - 1) / C::WAVES : 0;
+        // blocks of this wave: b0 + w + WAVES*t, t < nb_w
+        const int nb_w = b1 - b0 - w > 0 ? (b1 - b0 - w + WAVES - 1) / WAVES : 0;
         auto issue = [&](int t, int pb) {
             pb = (unsigned)pb < nblocks_pool ? pb : 0;
             const char *kp = kbase + (int64_t)pb * blk_bytes;
@@ -401,25 +413,25 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a)
             for (int j = 0; j < ROUNDS; ++j)
 #pragma unroll
                 for (int c = 0; c < CPL; ++c)
-                    dma16(kp + koff[j][c], st + (j * CPL + c) * 1024);
+                    dma16(kp + (size_t)koff[j][c], st + (j * CPL + c) * 1024);
 #pragma unroll
             for (int v = 0; v < VPASS; ++v)
-                dma16(vp + voff[v], st + KB + v * 1024);
+                dma16(vp + (size_t)voff[v], st + KB + v * 1024);
         };
         // prologue: NSTAGE - 1 blocks in flight
 #pragma unroll
         for (int t = 0; t < NSTAGE - 1; ++t)
             if (t < nb_w)
-                issue(t, uniform(table[b0 + w + 4 * t]));
-        int pb_ahead = NSTAGE - 1 < nb_w ? uniform(table[b0 + w + 4 * (NSTAGE - 1)]) : 0;
+                issue(t, uniform(table[b0 + w + WAVES * t]));
+        int pb_ahead = NSTAGE - 1 < nb_w ? uniform(table[b0 + w + WAVES * (NSTAGE - 1)]) : 0;
 
         for (int t = 0; t < nb_w; ++t) {
-            const int b = b0 + w + 4 * t;
+            const int b = b0 + w + WAVES * t;
             // keep NSTAGE - 1 blocks ahead in flight; fetch the next table entry early
             if (t + NSTAGE - 1 < nb_w) {
                 issue(t + NSTAGE - 1, pb_ahead);
                 if (t + NSTAGE < nb_w)
-                    pb_ahead = uniform(table[b + 4 * NSTAGE]);
+                    pb_ahead = uniform(table[b + WAVES * NSTAGE]);
             }
             const int after = nb_w - 1 - t < NSTAGE - 1 ? nb_w - 1 - t : NSTAGE - 1;
             wait_blocks_after<LPB, NSTAGE>(after);
@@ -519,13 +531,21 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a)
             __builtin_amdgcn_wave_barrier();
 
             // -- PV ----------------------------------------------------------
-            const bool partial = tbase + 16 > L;
+            u32x4 vrow[VPASS];
+#pragma unroll
+            for (int v = 0; v < VPASS; ++v)
+                vrow[v] = *(const u32x4 *)(st + KB + v * 1024);
+            if (tbase + 16 > L) {  // last block of the sequence (wave-uniform): slots past
+                                   // the context may hold any bits, their p is 0
+#pragma unroll
+                for (int v = 0; v < VPASS; ++v)
+                    if (tbase + row_token<LPT>(row, v * VTPR + vh) >= L)
+                        vrow[v] = u32x4{0u, 0u, 0u, 0u};
+            }
 #pragma unroll
             for (int v = 0; v < VPASS; ++v) {
                 const int tk = row_token<LPT>(row, v * VTPR + vh);
-                u32x4 vv = *(const u32x4 *)(st + KB + v * 1024);
-                if (partial && tbase + tk >= L)
-                    vv = u32x4{0u, 0u, 0u, 0u};
+                const u32x4 vv = vrow[v];
                 float pr[G];
 #pragma unroll
                 for (int h = 0; h < G; ++h)
@@ -599,16 +619,16 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a)
         }
         __syncthreads();
 
-        // ---- merge the four waves; write output or a partial --------------
-        for (int e = tid; e < G * D; e += 256) {
+        // ---- merge the waves; write the output, or a partial -----------------
+        for (int e = tid; e < G * D; e += NT) {
             const int h = e / D, c = e - h * D;
             float M = -INFINITY;
 #pragma unroll
-            for (int ww = 0; ww < C::WAVES; ++ww)
+            for (int ww = 0; ww < WAVES; ++ww)
                 M = fmaxf(M, sm.msum[ww][0][h]);
             float A = 0.f, Ls = 0.f;
 #pragma unroll
-            for (int ww = 0; ww < C::WAVES; ++ww) {
+            for (int ww = 0; ww < WAVES; ++ww) {
                 const float m = sm.msum[ww][0][h];
                 const float f = m == -INFINITY ? 0.f : fast_exp2(m - M);
                 A += f * sm.acc[ww][h][c];
@@ -617,18 +637,65 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a)
             if (direct) {
                 a.out[((int64_t)i * Hq + g * G + h) * D + c] = A / Ls * a.v_scale;
             } else {
-                a.ws_acc[((int64_t)slot * G + h) * D + c] = A;
+                // partials are written and read with device-coherent (L2-bypassing)
+                // accesses, so the hand-over below needs no cache flush
+                coherent_store(&a.ws_acc[((int64_t)slot * G + h) * D + c], A);
                 if (c == 0) {
-                    a.ws_ml[((int64_t)slot * G + h) * 2 + 0] = M;
-                    a.ws_ml[((int64_t)slot * G + h) * 2 + 1] = Ls;
+                    coherent_store(&a.ws_ml[((int64_t)slot * G + h) * 2 + 0], M);
+                    coherent_store(&a.ws_ml[((int64_t)slot * G + h) * 2 + 1], Ls);
                 }
             }
         }
-        if (tid == 0) {
-            if (first)
-                a.ws_lohi[((int64_t)i * Hkv + g) * 2 + 0] = slot;
-            if (last)
-                a.ws_lohi[((int64_t)i * Hkv + g) * 2 + 1] = slot;
+        if (!direct) {
+            // The partial slots of (i, g) are the contiguous range [lo, hi].  Count
+            // arrivals; the work-group that completes the count merges every
+            // partial of (i, g) and writes the output.  Ordering: every wave waits
+            // for its coherent partial stores to complete before the barrier that
+            // precedes the count, and the merger reads them with coherent loads
+            // issued after it has seen the final count.
+            const int pair = i * Hkv + g;
+            int lo, hi;
+            if (PB > 0) {
+                lo = (int)(item - x);
+                hi = lo + n_i - 1;
+            } else {
+                const long long W = gridDim.x;
+                const long long first_item = base_i + (long long)g * n_i;
+                const long long last_item = first_item + n_i - 1;
+                const long long k_first = ((first_item + 1) * W - 1) / total;
+                const long long k_last = ((last_item + 1) * W - 1) / total;
+                const long long r_first = k_first < k_first * total / W ? k_first : k_first * total / W;
+                const long long r_last = k_last < k_last * total / W ? k_last : k_last * total / W;
+                lo = (int)r_first + pair;
+                hi = (int)r_last + pair;
+            }
+            wait_vm<0>();
+            __syncthreads();
+            if (tid == 0)
+                sm.last = __hip_atomic_fetch_add(&a.ws_count[pair], 1, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT) == hi - lo;
+            __syncthreads();
+            if (sm.last) {
+                for (int e = tid; e < G * D; e += NT) {
+                    const int h = e / D;
+                    const float *ml = a.ws_ml + ((int64_t)lo * G + h) * 2;
+                    const float *src = a.ws_acc + (int64_t)lo * G * D + e;
+                    float M = -INFINITY;
+                    for (int s2 = 0; s2 <= hi - lo; ++s2)
+                        M = fmaxf(M, coherent_load(&ml[(int64_t)s2 * G * 2]));
+                    float num = 0.f, den = 0.f;
+#pragma unroll 4
+                    for (int s2 = 0; s2 <= hi - lo; ++s2) {
+                        const float m = coherent_load(&ml[(int64_t)s2 * G * 2]);
+                        const float f = m == -INFINITY ? 0.f : fast_exp2(m - M);
+                        num += f * coherent_load(&src[(int64_t)s2 * G * D]);
+                        den += f * coherent_load(&ml[(int64_t)s2 * G * 2 + 1]);
+                    }
+                    a.out[((int64_t)i * Hq + g * G) * D + e] = num / den * a.v_scale;
+                }
+                if (tid == 0)
+                    a.ws_count[pair] = 0;  // leave the counter at zero for the next call
+            }
         }
         __syncthreads();
 
@@ -639,47 +706,6 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a)
             ++i;
         }
     }
-}
-
-// Merge the partial results of every (sequence, KV head) that was split:
-// out = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s, M = max_s m_s.
-// One work-group per (sequence, KV head), one thread per output element; the
-// slot loop is unrolled so its loads are in flight together.
-template <int D, int G>
-__global__ __launch_bounds__(1024) void decode_reduce_kernel(DecodeArgs a)
-{
-    const int Hkv = a.num_kv_heads, Hq = a.num_q_heads;
-    const int pair = blockIdx.x;
-    const int i = pair / Hkv, g = pair - (pair / Hkv) * Hkv;
-    const int e = threadIdx.x;
-    const int L = scalar_view(a.context_lens)[i];
-    float *out = a.out + ((int64_t)i * Hq + g * G) * D;
-    if (e >= G * D)
-        return;
-    if (L <= 0) {
-        out[e] = 0.f;
-        return;
-    }
-    const int lo = scalar_view(a.ws_lohi)[(int64_t)pair * 2 + 0];
-    const int hi = scalar_view(a.ws_lohi)[(int64_t)pair * 2 + 1];
-    if (lo == hi)
-        return;
-    const int h = e / D;
-    const float *ml = a.ws_ml + ((int64_t)lo * G + h) * 2;
-    const float *acc = a.ws_acc + (int64_t)lo * G * D + e;
-    const int np = hi - lo + 1;
-    float M = -INFINITY;
-    for (int s = 0; s < np; ++s)
-        M = fmaxf(M, ml[(int64_t)s * G * 2]);
-    float num = 0.f, den = 0.f;
-#pragma unroll 4
-    for (int s = 0; s < np; ++s) {
-        const float m = ml[(int64_t)s * G * 2];
-        const float f = m == -INFINITY ? 0.f : fast_exp2(m - M);
-        num += f * acc[(int64_t)s * G * D];
-        den += f * ml[(int64_t)s * G * 2 + 1];
-    }
-    out[e] = num / den * a.v_scale;
 }
 
 int64_t decode_partial_slots(int num_seqs, int num_kv_heads, int max_blocks, int part_blocks,
@@ -707,8 +733,8 @@ bool decode_supported(int cache_dtype, int head_dim, int group)
 template <int CDT, int D, int G>
 static DecodeKernels kernels_t()
 {
-    return DecodeKernels{(const void *)decode_kernel<CDT, D, G, DECODE_STAGES>,
-                         (const void *)decode_reduce_kernel<D, G>};
+    return DecodeKernels{(const void *)decode_kernel<CDT, D, G, DECODE_STAGES, DECODE_WAVES>,
+                         64 * DECODE_WAVES};
 }
 
 template <int CDT, int D>
@@ -748,13 +774,7 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream)
     const DecodeKernels k = decode_kernels(a.cache_dtype, a.head_dim, a.num_q_heads / a.num_kv_heads);
     DecodeArgs args = a;
     void *params[] = {&args};
-    hipError_t e = hipLaunchKernel(k.main, dim3(a.grid), dim3(256), params, 0, stream);
-    if (e != hipSuccess)
-        return e;
-    const int G = a.num_q_heads / a.num_kv_heads;
-    const unsigned threads = (unsigned)((G * a.head_dim + 63) / 64 * 64);
-    return hipLaunchKernel(k.reduce, dim3(a.num_seqs * a.num_kv_heads), dim3(threads), params, 0,
-                           stream);
+    return hipLaunchKernel(k.main, dim3(a.grid), dim3(k.threads), params, 0, stream);
 }
 
 }  // namespace pa

@@ -72,7 +72,8 @@ int decode_grid(const pa_shape *s)
     if (slot == 0) {
         int per_cu = 0;
         const pa::DecodeKernels k = pa::decode_kernels(dt, s->head_dim, G);
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k.main, 256, 0) != hipSuccess ||
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k.main, k.threads, 0) !=
+                hipSuccess ||
             per_cu <= 0)
             per_cu = 1;
         slot = per_cu * device_cus();
@@ -114,7 +115,7 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct DecodeLayout {
     int64_t slots;
-    size_t acc_bytes, ml_bytes, lohi_bytes, total;
+    size_t count_bytes, acc_bytes, ml_bytes, total;
 };
 
 DecodeLayout decode_layout(const pa_shape *s)
@@ -124,10 +125,10 @@ DecodeLayout decode_layout(const pa_shape *s)
     DecodeLayout L;
     L.slots = pa::decode_partial_slots(s->num_seqs, s->num_kv_heads, s->max_blocks_per_seq, pb,
                                        decode_grid(s));
-    L.acc_bytes = align256((size_t)L.slots * G * s->head_dim * sizeof(float));
+    L.count_bytes = (size_t)pa::kDecodeCounterSlots * sizeof(int32_t);
     L.ml_bytes = align256((size_t)L.slots * G * 2 * sizeof(float));
-    L.lohi_bytes = align256((size_t)s->num_seqs * s->num_kv_heads * 2 * sizeof(int32_t));
-    L.total = L.acc_bytes + L.ml_bytes + L.lohi_bytes;
+    L.acc_bytes = align256((size_t)L.slots * G * s->head_dim * sizeof(float));
+    L.total = L.count_bytes + L.ml_bytes + L.acc_bytes;
     return L;
 }
 
@@ -212,6 +213,9 @@ pa_status pa_decode(float *out, const void *q, const void *k_cache, const void *
         return fail(PA_ERR_INVALID, "partition_tokens must be 0 or a positive multiple of 16");
     if (!std::isfinite(scale))
         return fail(PA_ERR_INVALID, "scale is not finite");
+    if ((int64_t)shape->num_seqs * shape->num_kv_heads > pa::kDecodeCounterSlots)
+        return fail(PA_ERR_UNSUPPORTED, "num_seqs * num_kv_heads above %lld",
+                    (long long)pa::kDecodeCounterSlots);
     if (shape->num_seqs == 0)
         return ok();
     if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
@@ -240,9 +244,9 @@ pa_status pa_decode(float *out, const void *q, const void *k_cache, const void *
     a.qk_scale = scale * 1.4426950408889634f * kvs;
     a.v_scale = kvs;
     char *ws = (char *)workspace;
-    a.ws_acc = (float *)ws;
-    a.ws_ml = (float *)(ws + L.acc_bytes);
-    a.ws_lohi = (int32_t *)(ws + L.acc_bytes + L.ml_bytes);
+    a.ws_count = (int32_t *)ws;
+    a.ws_ml = (float *)(ws + L.count_bytes);
+    a.ws_acc = (float *)(ws + L.count_bytes + L.ml_bytes);
     hipError_t e = pa::launch_decode(a, (hipStream_t)stream);
     return e == hipSuccess ? ok() : hip_fail(e, "decode launch");
 }

@@ -94,6 +94,17 @@ __device__ __forceinline__ const __attribute__((address_space(4))) T *scalar_vie
 // Make the compiler materialise a loaded value here (waiting for its load).
 __device__ __forceinline__ void settle(uint32_t v) { asm volatile("" ::"v"(v)); }
 
+// Device-coherent accesses: agent-scope relaxed atomics, which gfx950 performs
+// at the coherence point shared by all XCDs (no L2 write-back or invalidate).
+__device__ __forceinline__ void coherent_store(float *p, float v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float coherent_load(const float *p)
+{
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 __device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

@@ -34,15 +34,18 @@ struct DecodeArgs {
     float v_scale;         // 1, or kv_scale for fp8 V
     float *ws_acc;         // [slots][G][D]
     float *ws_ml;          // [slots][G][2]
-    int32_t *ws_lohi;      // [S * Hkv][2]
+    int32_t *ws_count;     // [S * Hkv] arrival counters, zero between calls
 };
+// Arrival counters sit at the start of every decode workspace; this region
+// must be zero before the first call and every call leaves it zero.
+constexpr int64_t kDecodeCounterSlots = 1 << 20;
 // Number of partial-result slots the decode workspace must hold.
 int64_t decode_partial_slots(int num_seqs, int num_kv_heads, int max_blocks, int part_blocks,
                              int grid);
 bool decode_supported(int cache_dtype, int head_dim, int group);
 struct DecodeKernels {
-    const void *main;    // persistent split-K decode kernel
-    const void *reduce;  // partial-result merge
+    const void *main;    // persistent split-K decode kernel (merges its own partials)
+    int threads;         // work-group size
 };
 DecodeKernels decode_kernels(int cache_dtype, int head_dim, int group);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
