@@ -142,8 +142,9 @@ size_t pa_prefill_workspace_bytes(const pa_shape *shape, int64_t total_query_row
  *                  [query_start[r], query_start[r+1]), n_r rows
  *   context_lens:  [num_seqs] int32 total cached tokens of each request, its
  *                  chunk included (the chunk is written before the call)
+ *   scale:         softmax scale, finite and > 0 (else PA_ERR_INVALID)
  *   Row j of request r attends keys [0, context_lens[r] - n_r + j].
- *   Requires a bf16 q and a bf16 or fp8 cache.
+ *   Requires a bf16 q, a bf16 or fp8 cache and at most 65535 requests.
  */
 pa_status pa_prefill_chunk(float *out, const void *q, const void *k_cache, const void *v_cache,
                            const int32_t *block_tables, const int32_t *query_start,

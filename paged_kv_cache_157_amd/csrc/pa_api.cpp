@@ -282,10 +282,16 @@ pa_status pa_prefill_chunk(float *out, const void *q, const void *k_cache, const
         return fail(PA_ERR_INVALID, "total_query_rows < 0");
     if (total_query_rows > (int64_t)1 << 24)
         return fail(PA_ERR_UNSUPPORTED, "more than 2^24 query rows");
-    if (!std::isfinite(scale))
-        return fail(PA_ERR_INVALID, "scale is not finite");
+    if (!std::isfinite(scale) || !(scale > 0.f))
+        return fail(PA_ERR_INVALID, "prefill scale must be finite and > 0");
+    if (shape->num_seqs > 65535)
+        return fail(PA_ERR_UNSUPPORTED, "more than 65535 prefill requests in one call");
     if (shape->num_seqs == 0 || total_query_rows == 0)
         return ok();
+    const int m_tiles = pa::prefill_m_tiles(total_query_rows, shape->num_q_heads, shape->num_kv_heads);
+    const int kv_splits = pa::prefill_kv_splits(total_query_rows, shape->num_q_heads);
+    if ((int64_t)m_tiles * shape->num_kv_heads * kv_splits > INT32_MAX)
+        return fail(PA_ERR_UNSUPPORTED, "prefill grid too large");
     if (!out || !q || !k_cache || !v_cache || !block_tables || !query_start || !context_lens)
         return fail(PA_ERR_INVALID, "NULL data pointer");
     const size_t need = pa_prefill_workspace_bytes(shape, total_query_rows);
@@ -308,7 +314,8 @@ pa_status pa_prefill_chunk(float *out, const void *q, const void *k_cache, const
     a.max_blocks = shape->max_blocks_per_seq;
     a.num_blocks = shape->num_blocks;
     a.cache_dtype = shape->cache_dtype;
-    a.kv_splits = pa::prefill_kv_splits(total_query_rows, shape->num_q_heads);
+    a.kv_splits = kv_splits;
+    a.m_tiles = m_tiles;
     const float kvs = kv_scale_of(shape);
     a.qk_scale = scale * 1.4426950408889634f * kvs;
     a.v_scale = kvs;

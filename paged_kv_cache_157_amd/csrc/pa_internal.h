@@ -60,12 +60,14 @@ struct PrefillArgs {
     int64_t num_blocks;
     int cache_dtype;
     int kv_splits;
+    int m_tiles;           // row tiles per (request, KV head), from the largest chunk
     float qk_scale, v_scale;
     float *ws_acc;         // [kv_splits][rows*Hq][D]
     float *ws_ml;          // [kv_splits][rows*Hq][2]
 };
 bool prefill_supported(int cache_dtype, int head_dim, int group);
 int prefill_kv_splits(int64_t total_rows, int num_q_heads);
+int prefill_m_tiles(int64_t total_rows, int num_q_heads, int num_kv_heads);
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);
 
 }  // namespace pa

@@ -293,3 +293,31 @@ def test_prefill_groups(G):
     ref = oracle.prefill(host_bits(qp), pool_rows(p["k_h"]), pool_rows(p["v_h"]), p["bt_h"], qs,
                          p["lens_h"], p["scale"])
     assert max_err(out.cpu().numpy(), ref) <= TOL["bf16"]
+
+
+# ----------------------------------------------------------------------------
+# peaked scores: scale 1 on d = 128 gives scores of standard deviation ~11, so
+# the running maximum keeps rising along the keys and the lazy rescale of the
+# accumulators runs with non-zero partial results
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("storage", ["bf16", "fp8"])
+def test_prefill_peaked_scores(storage):
+    p, qp, qs = _prefill_problem(21, [(700, 300), (0, 90)], 16, 4, 128, storage)
+    say(f"prefill peaked {storage}")
+    out = torch.full(qp.shape, float("nan"), dtype=torch.float32, device="cuda")
+    binding.prefill_chunk(out, qp, p["k"], p["v"], p["bt"], to_dev(qs), p["lens"], 1.0,
+                          kv_scale=p["kv_scale"])
+    torch.cuda.synchronize()
+    ref = oracle.prefill(host_bits(qp), pool_rows(p["k_h"]), pool_rows(p["v_h"]), p["bt_h"], qs,
+                         p["lens_h"], 1.0, kv_scale=p["kv_scale"])
+    assert max_err(out.cpu().numpy(), ref) <= TOL[storage]
+
+
+@pytest.mark.parametrize("storage", ["bf16", "fp8"])
+def test_decode_peaked_scores(storage):
+    p = random_problem(22, 6, 28, 4, 128, [1, 17, 300, 1000, 2049, 4000], 1200, storage)
+    p["scale"] = 1.0
+    say(f"decode peaked {storage}")
+    out = decode_problem(p)
+    assert max_err(out, oracle_problem(p)) <= TOL[storage]
