@@ -7,11 +7,11 @@
 //
 // Here the query tile makes QK^T a dense contraction, so it runs on the
 // matrix cores (v_mfma_f32_32x32x16_bf16):
-//   * A work-group (4 waves) owns 256 "query rows" = (position, head) pairs of
-//     one KV head (all G heads of a position are adjacent, so one K/V tile
-//     feeds every head of the group), and one slice of the key range.  Each
-//     wave holds 64 rows as two 32-row MFMA blocks, so every K or V fragment
-//     read from LDS feeds two matrix products.
+//   * A work-group (8 waves, two per SIMD so that one wave's softmax overlaps
+//     the other's matrix products) owns 256 "query rows" = (position, head)
+//     pairs of one KV head (all G heads of a position are adjacent, so one K/V
+//     tile feeds every head of the group), and one slice of the key range.
+//     Each wave holds one 32-row MFMA block.
 //   * Per 64-key tile, K and V rows are gathered through the block table.
 //     The loads for tile t+1 are issued into registers before tile t is
 //     computed and land in the other half of a double-buffered LDS tile
@@ -60,14 +60,15 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi)
 template <int D>
 struct PrefillCfg {
     static constexpr int KT = 64;              // keys per tile
-    static constexpr int WAVES = 4;
-    static constexpr int MROWS = 64 * WAVES;   // query rows per work-group
+    static constexpr int WAVES = 8;            // two per SIMD
+    static constexpr int MROWS = 32 * WAVES;   // query rows per work-group
     static constexpr int ST = D / 16;          // 16-d steps of the QK contraction
     static constexpr int NKF = 2 * ST;         // 1 KiB K fragments per tile
-    static constexpr int KCH = NKF / WAVES;    // K fragments each wave stages
+    static constexpr int KWAVES = WAVES / 2;   // waves that stage K (the others stage V)
+    static constexpr int KCH = NKF / KWAVES;   // K fragments each K-staging wave loads
     static constexpr int NVI = (KT / 4) * (D / 8);  // V staging items (4 keys x 8 d)
     static constexpr int VSTR = KT + 8;        // bf16 per V^T row in LDS (padded)
-    static_assert(NKF % WAVES == 0 && NVI <= 64 * WAVES, "tile shape");
+    static_assert(NKF % KWAVES == 0 && NVI <= 64 * (WAVES - KWAVES), "tile shape");
 };
 
 template <int D>
@@ -77,7 +78,7 @@ struct PrefillSmem {
     __attribute__((aligned(16))) uint16_t k[2][C::KT * D];     // [buffer][fragment][lane][8]
     __attribute__((aligned(16))) uint16_t vt[2][D * C::VSTR];  // [buffer][d][key position]
     float alpha[C::WAVES][32];
-    float ml[C::WAVES][2][2][32];   // [wave][block][max, sum][row]
+    float ml[C::WAVES][2][32];      // [wave][max, sum][row]
 };
 
 // Position of key k (0..63) in a V^T row: inside each 16-key step the order is
@@ -114,7 +115,7 @@ __device__ __forceinline__ u32x4 widen(u32x2 x)
 }
 
 template <int CDT, int D>
-__global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a)
+__global__ __launch_bounds__(64 * PrefillCfg<D>::WAVES) void prefill_kernel(PrefillArgs a)
 {
     using C = PrefillCfg<D>;
     using Raw = typename RawChunk<CDT>::T;
@@ -147,20 +148,18 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a)
         return;
     const int pos_end = pos0 + ppt < n ? pos0 + ppt : n;
 
-    // this lane's query row in each of its two 32-row blocks (column of S^T)
-    int lim[2];
-    u32x4 qb[2][ST];
-#pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
-        const int mrow = 64 * w + 32 * cb + col;
-        const int pos = pos0 + mrow / G;
-        const int head = g * G + mrow % G;
-        const bool ok = mrow < ppt * G && pos < pos_end;
-        lim[cb] = ok ? P + pos : -1;  // last key this row attends
-        const uint16_t *qp = (const uint16_t *)a.q + ((int64_t)(qs + pos) * Hq + head) * D;
+    // this lane's query row (column of S^T) and its Q^T fragments
+    const int mrow = 32 * w + col;
+    const int my_pos = pos0 + mrow / G;
+    const int my_head = g * G + mrow % G;
+    const bool row_ok = mrow < ppt * G && my_pos < pos_end;
+    const int lim = row_ok ? P + my_pos : -1;  // last key this row attends
+    u32x4 qb[ST];
+    {
+        const uint16_t *qp = (const uint16_t *)a.q + ((int64_t)(qs + my_pos) * Hq + my_head) * D;
 #pragma unroll
         for (int s = 0; s < ST; ++s)
-            qb[cb][s] = ok ? *(const u32x4 *)(qp + 16 * s + 8 * hl) : u32x4{0u, 0u, 0u, 0u};
+            qb[s] = row_ok ? *(const u32x4 *)(qp + 16 * s + 8 * hl) : u32x4{0u, 0u, 0u, 0u};
     }
 
     // key tiles of this split
@@ -171,13 +170,11 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a)
     const int tmax = (P + pos_end - 1) / KT + 1;
     t1 = t1 < tmax ? t1 : tmax;
 
-    f32x16 o[2][D / 32];
+    f32x16 o[D / 32];
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt)
-            o[cb][dt] = f32x16{};
-    float mref[2] = {-INFINITY, -INFINITY}, lsum[2] = {0.f, 0.f};
+    for (int dt = 0; dt < D / 32; ++dt)
+        o[dt] = f32x16{};
+    float mref = -INFINITY, lsum = 0.f;
 
     const auto tab = scalar_view(a.block_tables + (int64_t)r * a.max_blocks);
     const int64_t tok_bytes = (int64_t)Hkv * D * EB;
@@ -186,7 +183,10 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a)
     const float c = a.qk_scale;
 
     // ---- staging: tile kt -> registers -> LDS buffer --------------------------
-    Raw kraw[C::KCH], vraw[4];
+    // Waves [KWAVES, WAVES) gather K fragments, the others gather V (4 keys x 8 d
+    // per thread); either way a thread holds four 16-byte chunks in flight.
+    const bool kstager = w >= C::KWAVES;
+    Raw stg[4];
     auto issue_loads = [&](int kt) {
         int pb[4];
 #pragma unroll
@@ -197,41 +197,44 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a)
                 e = tab[blk];
             pb[i] = (unsigned)e < (unsigned)a.num_blocks ? e : 0;
         }
+        if (kstager) {
 #pragma unroll
-        for (int j = 0; j < C::KCH; ++j) {
-            const int f = w + C::WAVES * j;  // fragment = (key half, d step)
-            const int key = (f / ST) * 32 + col;
-            const int ch = 2 * (f % ST) + hl;
-            const int kb = key >> 4;
-            const int p = kb == 0 ? pb[0] : kb == 1 ? pb[1] : kb == 2 ? pb[2] : pb[3];
-            kraw[j] = load_chunk<CDT>(kbase + ((int64_t)p * 16 + (key & 15)) * tok_bytes + ch * 8 * EB);
-        }
-        if (tid < C::NVI) {
+            for (int j = 0; j < C::KCH; ++j) {
+                const int f = (w - C::KWAVES) + C::KWAVES * j;  // (key half, d step)
+                const int key = (f / ST) * 32 + col;
+                const int ch = 2 * (f % ST) + hl;
+                const int kb = key >> 4;
+                const int p = kb == 0 ? pb[0] : kb == 1 ? pb[1] : kb == 2 ? pb[2] : pb[3];
+                stg[j] = load_chunk<CDT>(kbase + ((int64_t)p * 16 + (key & 15)) * tok_bytes +
+                                         ch * 8 * EB);
+            }
+        } else if (tid < C::NVI) {
             const int quad = tid & 15, vch = tid >> 4;
             const int kb = quad >> 2;
             const int p = kb == 0 ? pb[0] : kb == 1 ? pb[1] : kb == 2 ? pb[2] : pb[3];
             const char *src = vbase + ((int64_t)p * 16 + 4 * (quad & 3)) * tok_bytes + vch * 8 * EB;
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk)
-                vraw[kk] = load_chunk<CDT>(src + kk * tok_bytes);
+                stg[kk] = load_chunk<CDT>(src + kk * tok_bytes);
         }
         // keep the loads ahead of the compute that follows
         asm volatile("" ::: "memory");
     };
     auto write_stage = [&](int bi, int kt) {
+        if (kstager) {
 #pragma unroll
-        for (int j = 0; j < C::KCH; ++j) {
-            const int f = w + C::WAVES * j;
-            *(u32x4 *)&sm.k[bi][(f * 64 + lane) * 8] = widen(kraw[j]);
-        }
-        if (tid < C::NVI) {
+            for (int j = 0; j < C::KCH; ++j) {
+                const int f = (w - C::KWAVES) + C::KWAVES * j;
+                *(u32x4 *)&sm.k[bi][(f * 64 + lane) * 8] = widen(stg[j]);
+            }
+        } else if (tid < C::NVI) {
             const int quad = tid & 15, vch = tid >> 4;
             u32x4 rows[4];
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) {
                 // V rows past the context are zero (0 * garbage must not reach O)
                 const bool ok = kt * KT + 4 * quad + kk < Ctx;
-                rows[kk] = ok ? widen(vraw[kk]) : u32x4{0u, 0u, 0u, 0u};
+                rows[kk] = ok ? widen(stg[kk]) : u32x4{0u, 0u, 0u, 0u};
             }
             const int pos = vt_pos(4 * quad);
 #pragma unroll
@@ -261,86 +264,73 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a)
         const bool full = key0 + KT <= Ctx && key0 + KT - 1 <= P + pos0;
 #pragma unroll
         for (int kc = 0; kc < 2; ++kc) {
-            // ---- S^T = K Q^T for one 32-key half, both 32-row blocks ---------------
-            f32x16 s[2] = {f32x16{}, f32x16{}};
+            // ---- S^T = K Q^T for one 32-key half ------------------------------------
+            f32x16 s = f32x16{};
 #pragma unroll
             for (int st = 0; st < ST; ++st) {
                 const u32x4 ka = *(const u32x4 *)&sm.k[bi][((kc * ST + st) * 64 + lane) * 8];
-#pragma unroll
-                for (int cb = 0; cb < 2; ++cb)
-                    s[cb] = mfma32(ka, qb[cb][st], s[cb]);
+                s = mfma32(ka, qb[st], s);
             }
 
-            // ---- mask (diagonal / ragged tiles only), row maxima, lazy rescale ---
-            float mu[2];
+            // ---- mask (diagonal / ragged tiles only), row maximum, lazy rescale ----
+            if (!full) {
 #pragma unroll
-            for (int cb = 0; cb < 2; ++cb) {
-                if (!full) {
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const int key = key0 + 32 * kc + 8 * (i >> 2) + 4 * hl + (i & 3);
-                        s[cb][i] = key <= lim[cb] ? s[cb][i] : -INFINITY;
-                    }
+                for (int i = 0; i < 16; ++i) {
+                    const int key = key0 + 32 * kc + 8 * (i >> 2) + 4 * hl + (i & 3);
+                    s[i] = key <= lim ? s[i] : -INFINITY;
                 }
-                float tm = -INFINITY;
-#pragma unroll
-                for (int i = 0; i < 16; ++i)
-                    tm = fmaxf(tm, s[cb][i]);
-                tm = fmaxf(tm, __shfl_xor(tm, 32)) * c;  // c > 0: scaled maximum
-                if (wave_any(tm > mref[cb] + TAU)) {
-                    const float mnew = fmaxf(mref[cb], tm);
-                    const float alpha = mnew == -INFINITY ? 1.f : fast_exp2(mref[cb] - mnew);
-                    lsum[cb] *= alpha;
-                    mref[cb] = mnew;
-                    if (hl == 0)
-                        sm.alpha[w][col] = alpha;
-                    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-                    __builtin_amdgcn_wave_barrier();
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const float al = sm.alpha[w][8 * (i >> 2) + 4 * hl + (i & 3)];
-#pragma unroll
-                        for (int dt = 0; dt < D / 32; ++dt)
-                            o[cb][dt][i] *= al;
-                    }
-                    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-                    __builtin_amdgcn_wave_barrier();
-                }
-                // a row with no valid key yet keeps mref = -inf: its probabilities are 0
-                mu[cb] = mref[cb] == -INFINITY ? 0.f : mref[cb];
             }
+            float tm = -INFINITY;
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                tm = fmaxf(tm, s[i]);
+            tm = fmaxf(tm, __shfl_xor(tm, 32)) * c;  // c > 0: scaled maximum
+            if (wave_any(tm > mref + TAU)) {
+                const float mnew = fmaxf(mref, tm);
+                const float alpha = mnew == -INFINITY ? 1.f : fast_exp2(mref - mnew);
+                lsum *= alpha;
+                mref = mnew;
+                if (hl == 0)
+                    sm.alpha[w][col] = alpha;
+                __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const float al = sm.alpha[w][8 * (i >> 2) + 4 * hl + (i & 3)];
+#pragma unroll
+                    for (int dt = 0; dt < D / 32; ++dt)
+                        o[dt][i] *= al;
+                }
+                __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+            }
+            // a row with no valid key yet keeps mref = -inf: its probabilities are 0
+            const float mu = mref == -INFINITY ? 0.f : mref;
 
-            // ---- probabilities (bf16 head + tail) and O += P V ----------------------
+            // ---- probabilities (bf16 head + tail) and O += P V ------------------------
 #pragma unroll
             for (int h8 = 0; h8 < 2; ++h8) {
                 const int ks = 2 * kc + h8;  // 16-key step of the tile
-                u32x4 ph[2], pl[2];
+                float p[8];
 #pragma unroll
-                for (int cb = 0; cb < 2; ++cb) {
-                    float p[8];
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) {
-                        p[j] = fast_exp2(fmaf(s[cb][8 * h8 + j], c, -mu[cb]));
-                        lsum[cb] += p[j];
-                    }
-                    uint32_t h[4], t[4];
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        h[j] = pack_bf16(p[2 * j], p[2 * j + 1]);
-                        t[j] = pack_bf16(p[2 * j] - bf16_lo(h[j]), p[2 * j + 1] - bf16_hi(h[j]));
-                    }
-                    ph[cb] = u32x4{h[0], h[1], h[2], h[3]};
-                    pl[cb] = u32x4{t[0], t[1], t[2], t[3]};
+                for (int j = 0; j < 8; ++j) {
+                    p[j] = fast_exp2(fmaf(s[8 * h8 + j], c, -mu));
+                    lsum += p[j];
                 }
+                uint32_t h[4], t[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    h[j] = pack_bf16(p[2 * j], p[2 * j + 1]);
+                    t[j] = pack_bf16(p[2 * j] - bf16_lo(h[j]), p[2 * j + 1] - bf16_hi(h[j]));
+                }
+                const u32x4 ph = u32x4{h[0], h[1], h[2], h[3]};
+                const u32x4 pl = u32x4{t[0], t[1], t[2], t[3]};
 #pragma unroll
                 for (int dt = 0; dt < D / 32; ++dt) {
                     const u32x4 vb =
                         *(const u32x4 *)&sm.vt[bi][(32 * dt + col) * VSTR + 16 * ks + 8 * hl];
-#pragma unroll
-                    for (int cb = 0; cb < 2; ++cb) {
-                        o[cb][dt] = mfma32(ph[cb], vb, o[cb][dt]);
-                        o[cb][dt] = mfma32(pl[cb], vb, o[cb][dt]);
-                    }
+                    o[dt] = mfma32(ph, vb, o[dt]);
+                    o[dt] = mfma32(pl, vb, o[dt]);
                 }
             }
         }
@@ -351,68 +341,70 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a)
     }
 
     // ---- finish: row sums, then normalise or store a partial ------------------
-#pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
-        lsum[cb] += __shfl_xor(lsum[cb], 32);
-        if (hl == 0) {
-            sm.ml[w][cb][0][col] = mref[cb];
-            sm.ml[w][cb][1][col] = lsum[cb];
-        }
+    lsum += __shfl_xor(lsum, 32);
+    if (hl == 0) {
+        sm.ml[w][0][col] = mref;
+        sm.ml[w][1][col] = lsum;
     }
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     __builtin_amdgcn_wave_barrier();
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb)
+    for (int i = 0; i < 16; ++i) {
+        const int orow = 8 * (i >> 2) + 4 * hl + (i & 3);
+        const int mr = 32 * w + orow;
+        const int pos = pos0 + mr / G;
+        if (mr >= ppt * G || pos >= pos_end)
+            continue;
+        const int head = g * G + mr % G;
+        const int64_t qrow = (int64_t)(qs + pos) * Hq + head;
+        const float m = sm.ml[w][0][orow], l = sm.ml[w][1][orow];
+        if (KS == 1) {
+            const float inv = a.v_scale / l;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int orow = 8 * (i >> 2) + 4 * hl + (i & 3);
-            const int mr = 64 * w + 32 * cb + orow;
-            const int pos = pos0 + mr / G;
-            if (mr >= ppt * G || pos >= pos_end)
-                continue;
-            const int head = g * G + mr % G;
-            const int64_t qrow = (int64_t)(qs + pos) * Hq + head;
-            const float m = sm.ml[w][cb][0][orow], l = sm.ml[w][cb][1][orow];
-            if (KS == 1) {
-                const float inv = a.v_scale / l;
+            for (int dt = 0; dt < D / 32; ++dt)
+                a.out[qrow * D + 32 * dt + col] = o[dt][i] * inv;
+        } else {
+            float *dst = a.ws_acc + ((int64_t)split * a.total_rows * Hq + qrow) * D;
 #pragma unroll
-                for (int dt = 0; dt < D / 32; ++dt)
-                    a.out[qrow * D + 32 * dt + col] = o[cb][dt][i] * inv;
-            } else {
-                float *dst = a.ws_acc + ((int64_t)split * a.total_rows * Hq + qrow) * D;
-#pragma unroll
-                for (int dt = 0; dt < D / 32; ++dt)
-                    dst[32 * dt + col] = o[cb][dt][i];
-                if (col == 0) {
-                    float *ml = a.ws_ml + ((int64_t)split * a.total_rows * Hq + qrow) * 2;
-                    ml[0] = m;
-                    ml[1] = l;
-                }
+            for (int dt = 0; dt < D / 32; ++dt)
+                dst[32 * dt + col] = o[dt][i];
+            if (col == 0) {
+                float *ml = a.ws_ml + ((int64_t)split * a.total_rows * Hq + qrow) * 2;
+                ml[0] = m;
+                ml[1] = l;
             }
         }
+    }
 }
 
+// Merge of the key-range splits: thread = (query row, 4 consecutive d).
 template <int D>
 __global__ __launch_bounds__(256) void prefill_reduce_kernel(PrefillArgs a)
 {
+    typedef __attribute__((ext_vector_type(4))) float f32x4;
     const int64_t rows = a.total_rows * a.num_q_heads;
     const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (e >= rows * D)
+    if (e >= rows * (D / 4))
         return;
-    const int64_t qrow = e / D;
+    const int64_t qrow = e / (D / 4);
+    const int d4 = (int)(e - qrow * (D / 4)) * 4;
     const int KS = a.kv_splits;
-    const int64_t stride = rows;
     float M = -INFINITY;
     for (int s = 0; s < KS; ++s)
-        M = fmaxf(M, a.ws_ml[(s * stride + qrow) * 2]);
-    float num = 0.f, den = 0.f;
+        M = fmaxf(M, a.ws_ml[(s * rows + qrow) * 2]);
+    f32x4 num = f32x4{0.f, 0.f, 0.f, 0.f};
+    float den = 0.f;
     for (int s = 0; s < KS; ++s) {
-        const float m = a.ws_ml[(s * stride + qrow) * 2];
-        const float f = m == -INFINITY ? 0.f : fast_exp2(m - M);
-        num += f * a.ws_acc[(s * stride) * D + e];
-        den += f * a.ws_ml[(s * stride + qrow) * 2 + 1];
+        const f32x2 ml = *(const f32x2 *)&a.ws_ml[(s * rows + qrow) * 2];
+        const float f = ml[0] == -INFINITY ? 0.f : fast_exp2(ml[0] - M);
+        num += f * *(const f32x4 *)&a.ws_acc[(s * rows + qrow) * D + d4];
+        den += f * ml[1];
     }
-    a.out[e] = num / den * a.v_scale;
+    const float inv = a.v_scale / den;
+    float *dst = a.out + qrow * D + d4;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        dst[j] = num[j] * inv;
 }
 
 bool prefill_supported(int cache_dtype, int head_dim, int group)
@@ -445,11 +437,11 @@ template <int CDT, int D>
 static hipError_t launch_prefill_t(const PrefillArgs &a, hipStream_t stream)
 {
     dim3 grid((unsigned)(a.m_tiles * a.num_kv_heads * a.kv_splits), (unsigned)a.num_reqs);
-    prefill_kernel<CDT, D><<<grid, 256, 0, stream>>>(a);
+    prefill_kernel<CDT, D><<<grid, 64 * PrefillCfg<D>::WAVES, 0, stream>>>(a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.kv_splits == 1)
         return e;
-    const int64_t n = a.total_rows * a.num_q_heads * D;
+    const int64_t n = a.total_rows * a.num_q_heads * (D / 4);
     prefill_reduce_kernel<D><<<(unsigned)((n + 255) / 256), 256, 0, stream>>>(a);
     return hipGetLastError();
 }
