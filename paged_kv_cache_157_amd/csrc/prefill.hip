@@ -57,72 +57,116 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi)
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
 
-template <int D>
+constexpr int kPrefillWaves = 8;  // two per SIMD
+constexpr int kPrefillThreads = 64 * kPrefillWaves;
+
+template <int CDT, int D>
 struct PrefillCfg {
-    static constexpr int KT = 64;              // keys per tile
-    static constexpr int WAVES = 8;            // two per SIMD
-    static constexpr int MROWS = 32 * WAVES;   // query rows per work-group
-    static constexpr int ST = D / 16;          // 16-d steps of the QK contraction
-    static constexpr int NKF = 2 * ST;         // 1 KiB K fragments per tile
-    static constexpr int KWAVES = WAVES / 2;   // waves that stage K (the others stage V)
-    static constexpr int KCH = NKF / KWAVES;   // K fragments each K-staging wave loads
-    static constexpr int NVI = (KT / 4) * (D / 8);  // V staging items (4 keys x 8 d)
-    static constexpr int VSTR = KT + 8;        // bf16 per V^T row in LDS (padded)
-    static_assert(NKF % KWAVES == 0 && NVI <= 64 * (WAVES - KWAVES), "tile shape");
+    static constexpr int KT = 64;                  // keys per tile
+    static constexpr int WAVES = kPrefillWaves;
+    static constexpr int MROWS = 32 * WAVES;       // query rows per work-group
+    static constexpr int ST = D / 16;              // 16-d steps of the QK contraction
+    static constexpr int ROWB = 2 * D;             // bytes of a bf16 K or V row in LDS
+    static constexpr int TILEB = KT * ROWB;        // bytes of a bf16 K (or V) tile
+    static constexpr bool RAW = CDT == DT_FP8;     // fp8 rows are loaded raw, widened in LDS
+    static constexpr int SROWB = RAW ? D : 2 * D;  // bytes of a row as cached
+    static constexpr int DMA_ROWS = 1024 / SROWB;  // rows per global->LDS instruction
+    static constexpr int DMA_TILE = 2 * KT / DMA_ROWS;  // instructions per tile (K, then V)
+    static constexpr int DPW = DMA_TILE / WAVES;   // instructions per wave per tile
+    static constexpr int NSTAGE = 4;               // tiles in the load ring
+    static constexpr int STAGEB = 2 * KT * SROWB;  // bytes of one ring stage (K tile, V tile)
+    static constexpr int CBUFB = RAW ? 2 * 2 * TILEB : 0;  // widened double buffer (fp8)
+    static constexpr int LDSB = NSTAGE * STAGEB + CBUFB;
+    static_assert(DMA_TILE % WAVES == 0 && DMA_ROWS <= 16 && 16 % DMA_ROWS == 0, "tile shape");
+    static_assert(LDSB <= 128 * 1024, "LDS budget");
 };
 
-template <int D>
+template <int CDT, int D>
 struct PrefillSmem {
-    using C = PrefillCfg<D>;
-    // 16-byte alignment lets the compiler use ds_read_b128 / ds_write_b128
-    __attribute__((aligned(16))) uint16_t k[2][C::KT * D];     // [buffer][fragment][lane][8]
-    __attribute__((aligned(16))) uint16_t vt[2][D * C::VSTR];  // [buffer][d][key position]
+    using C = PrefillCfg<CDT, D>;
+    __attribute__((aligned(1024))) char ring[C::LDSB];
     float alpha[C::WAVES][32];
-    float ml[C::WAVES][2][32];      // [wave][max, sum][row]
+    float ml[C::WAVES][2][32];  // [wave][max, sum][row]
 };
 
-// Position of key k (0..63) in a V^T row: inside each 16-key step the order is
-// keys 0-3, 8-11, 4-7, 12-15, i.e. the order in which a lane half of the S^T
-// result holds them.
-__device__ __forceinline__ int vt_pos(int k)
+// XOR swizzles of the 16-byte chunk index inside a K / V row of the LDS tile.
+// K rows are read 16 bytes per lane, 32 consecutive keys at one chunk: key & 7
+// spreads any 8 of them over the 8 bank groups.  V rows are read with the
+// transposing 8-byte reads: a 16-lane group touches 4 consecutive keys x 2
+// adjacent chunks, which 2 * (key & 3) + ((key >> 2) & 1) keeps apart.
+__device__ __forceinline__ int swz_k(int key) { return key & 7; }
+__device__ __forceinline__ int swz_v(int key) { return ((key & 3) << 1) | ((key >> 2) & 1); }
+
+// One 16-byte chunk of bf16 (8 values) from 8 fp8 bytes, exactly.
+__device__ __forceinline__ u32x4 widen8(uint32_t w0, uint32_t w1)
 {
-    const int q = (k >> 2) & 3;
-    const int perm = (q == 0) ? 0 : (q == 1) ? 8 : (q == 2) ? 4 : 12;
-    return (k & ~15) + perm + (k & 3);
+    return u32x4{fp8x2_to_bf16x2<false>(w0), fp8x2_to_bf16x2<true>(w0), fp8x2_to_bf16x2<false>(w1),
+                 fp8x2_to_bf16x2<true>(w1)};
 }
 
-// One 16-byte chunk (8 elements) of a cached row as loaded, and widened to bf16.
-template <int CDT>
-struct RawChunk {
-    using T = u32x4;
-};
-template <>
-struct RawChunk<DT_FP8> {
-    using T = u32x2;
-};
-
-template <int CDT>
-__device__ __forceinline__ typename RawChunk<CDT>::T load_chunk(const char *p)
+// ds_read_b64_tr_b16: within each 16-lane group, lane i receives element i % 4
+// of the 4 x 16-bit values loaded by lanes i / 4, 4 + i / 4, 8 + i / 4 and
+// 12 + i / 4 (checked on gfx950 with an in-bounds probe), i.e. a 4 x 16 block
+// of a row-major tile arrives transposed.  Issued as inline assembly: the
+// compiler would otherwise wait for every outstanding global->LDS load before
+// it.  The result may only be used after lds_wait() has taken it as operand.
+__device__ __forceinline__ u32x2 lds_read_tr16(const char *p)
 {
-    return *(const typename RawChunk<CDT>::T *)p;
+    const uint32_t addr = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char *)p;
+    u32x2 r;
+    asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(addr) : "memory");
+    return r;
+}
+template <int N>
+__device__ __forceinline__ void lds_wait(u32x2 (&r)[N])
+{
+    static_assert(N == 4 || N == 8, "operand count");
+    if constexpr (N == 4)
+        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]));
+    else
+        asm volatile("s_waitcnt lgkmcnt(0)"
+                     : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]), "+v"(r[4]), "+v"(r[5]),
+                       "+v"(r[6]), "+v"(r[7]));
 }
 
-__device__ __forceinline__ u32x4 widen(u32x4 x) { return x; }
-__device__ __forceinline__ u32x4 widen(u32x2 x)
+// Work-group barrier that drains this wave's LDS operations only: the
+// global->LDS loads of later tiles stay in flight (__syncthreads would wait
+// for them too).
+__device__ __forceinline__ void barrier_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// s_waitcnt vmcnt(N): the global->LDS loads are counted there and the compiler
+// does not wait for them by itself.
+template <int N>
+__device__ __forceinline__ void wait_vm()
 {
-    return u32x4{fp8x2_to_bf16x2<false>(x[0]), fp8x2_to_bf16x2<true>(x[0]),
-                 fp8x2_to_bf16x2<false>(x[1]), fp8x2_to_bf16x2<true>(x[1])};
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+// wait until at most n tiles of this wave's loads (DPW instructions each) are
+// still in flight, n <= 2
+template <int DPW>
+__device__ __forceinline__ void wait_tiles_in_flight(int n)
+{
+    if (n >= 2)
+        wait_vm<2 * DPW>();
+    else if (n == 1)
+        wait_vm<DPW>();
+    else
+        wait_vm<0>();
+}
+
+__device__ __forceinline__ void dma16(const void *src, void *lds_dst)
+{
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)lds_dst, 16, 0, 0);
 }
 
 template <int CDT, int D>
-__global__ __launch_bounds__(64 * PrefillCfg<D>::WAVES) void prefill_kernel(PrefillArgs a)
+__global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
 {
-    using C = PrefillCfg<D>;
-    using Raw = typename RawChunk<CDT>::T;
-    constexpr int KT = C::KT, ST = C::ST, VSTR = C::VSTR;
+    using C = PrefillCfg<CDT, D>;
+    constexpr int KT = C::KT, ST = C::ST, ROWB = C::ROWB, NS = C::NSTAGE, DPW = C::DPW;
     constexpr int EB = Storage<CDT>::bytes;
     constexpr float TAU = 8.0f;
-    __shared__ PrefillSmem<D> sm;
+    __shared__ PrefillSmem<CDT, D> sm;
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int hl = lane >> 5, col = lane & 31;
@@ -160,6 +204,9 @@ __global__ __launch_bounds__(64 * PrefillCfg<D>::WAVES) void prefill_kernel(Pref
 #pragma unroll
         for (int s = 0; s < ST; ++s)
             qb[s] = row_ok ? *(const u32x4 *)(qp + 16 * s + 8 * hl) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int s = 0; s < ST; ++s)
+            settle(qb[s][0]);  // q is in registers before the counted loads start
     }
 
     // key tiles of this split
@@ -169,6 +216,7 @@ __global__ __launch_bounds__(64 * PrefillCfg<D>::WAVES) void prefill_kernel(Pref
     int t1 = t0 + tps < nkt ? t0 + tps : nkt;
     const int tmax = (P + pos_end - 1) / KT + 1;
     t1 = t1 < tmax ? t1 : tmax;
+    const int nt = t1 > t0 ? t1 - t0 : 0;
 
     f32x16 o[D / 32];
 #pragma unroll
@@ -182,12 +230,14 @@ __global__ __launch_bounds__(64 * PrefillCfg<D>::WAVES) void prefill_kernel(Pref
     const char *vbase = (const char *)a.v_cache + (int64_t)g * D * EB;
     const float c = a.qk_scale;
 
-    // ---- staging: tile kt -> registers -> LDS buffer --------------------------
-    // Waves [KWAVES, WAVES) gather K fragments, the others gather V (4 keys x 8 d
-    // per thread); either way a thread holds four 16-byte chunks in flight.
-    const bool kstager = w >= C::KWAVES;
-    Raw stg[4];
-    auto issue_loads = [&](int kt) {
+    // ---- global -> LDS: tile kt into ring stage s -----------------------------
+    // Instruction i of a tile moves DMA_ROWS rows of K (i < DMA_TILE / 2) or V;
+    // lane -> (row, 16-byte slot), fetching the source chunk that the row's
+    // swizzle puts in that slot (fp8 rows are copied unswizzled and widened
+    // later).  Rows past the context repeat the last context row, so every value
+    // that reaches the products is finite.
+    constexpr int SPR = C::SROWB / 16;  // 16-byte slots per cached row
+    auto issue_tile = [&](int kt, int s) {
         int pb[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -197,69 +247,52 @@ __global__ __launch_bounds__(64 * PrefillCfg<D>::WAVES) void prefill_kernel(Pref
                 e = tab[blk];
             pb[i] = (unsigned)e < (unsigned)a.num_blocks ? e : 0;
         }
-        if (kstager) {
+        const int last = Ctx - 1 - kt * KT;  // last context row of this tile (may exceed KT)
 #pragma unroll
-            for (int j = 0; j < C::KCH; ++j) {
-                const int f = (w - C::KWAVES) + C::KWAVES * j;  // (key half, d step)
-                const int key = (f / ST) * 32 + col;
-                const int ch = 2 * (f % ST) + hl;
-                const int kb = key >> 4;
-                const int p = kb == 0 ? pb[0] : kb == 1 ? pb[1] : kb == 2 ? pb[2] : pb[3];
-                stg[j] = load_chunk<CDT>(kbase + ((int64_t)p * 16 + (key & 15)) * tok_bytes +
-                                         ch * 8 * EB);
-            }
-        } else if (tid < C::NVI) {
-            const int quad = tid & 15, vch = tid >> 4;
-            const int kb = quad >> 2;
+        for (int j = 0; j < DPW; ++j) {
+            const int i = w + C::WAVES * j;
+            const bool isv = i >= C::DMA_TILE / 2;  // uniform
+            const int ii = isv ? i - C::DMA_TILE / 2 : i;
+            const int row = ii * C::DMA_ROWS + lane / SPR;
+            const int slot = lane % SPR;
+            const int key = row < last ? row : last;
+            const int kb = key >> 4;
             const int p = kb == 0 ? pb[0] : kb == 1 ? pb[1] : kb == 2 ? pb[2] : pb[3];
-            const char *src = vbase + ((int64_t)p * 16 + 4 * (quad & 3)) * tok_bytes + vch * 8 * EB;
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk)
-                stg[kk] = load_chunk<CDT>(src + kk * tok_bytes);
+            const int ch = C::RAW ? slot : slot ^ (isv ? swz_v(row) : swz_k(row));
+            const char *src = (isv ? vbase : kbase) + ((int64_t)p * 16 + (key & 15)) * tok_bytes + ch * 16;
+            dma16(src, sm.ring + s * C::STAGEB + (isv ? KT * C::SROWB : 0) + ii * 1024);
         }
-        // keep the loads ahead of the compute that follows
-        asm volatile("" ::: "memory");
     };
-    auto write_stage = [&](int bi, int kt) {
-        if (kstager) {
+    // fp8: widen ring stage s into compute buffer cb (bf16, swizzled rows)
+    auto widen_tile = [&](int s, int cb) {
+        constexpr int NCH = KT * D / 16;  // 16-byte raw chunks per K (or V) tile
 #pragma unroll
-            for (int j = 0; j < C::KCH; ++j) {
-                const int f = (w - C::KWAVES) + C::KWAVES * j;
-                *(u32x4 *)&sm.k[bi][(f * 64 + lane) * 8] = widen(stg[j]);
-            }
-        } else if (tid < C::NVI) {
-            const int quad = tid & 15, vch = tid >> 4;
-            u32x4 rows[4];
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                // V rows past the context are zero (0 * garbage must not reach O)
-                const bool ok = kt * KT + 4 * quad + kk < Ctx;
-                rows[kk] = ok ? widen(stg[kk]) : u32x4{0u, 0u, 0u, 0u};
-            }
-            const int pos = vt_pos(4 * quad);
-#pragma unroll
-            for (int x = 0; x < 4; ++x) {
-                // d = vch*8 + 2x (low halves) and vch*8 + 2x + 1 (high halves)
-                const uint32_t lo01 = __builtin_amdgcn_perm(rows[1][x], rows[0][x], 0x05040100u);
-                const uint32_t lo23 = __builtin_amdgcn_perm(rows[3][x], rows[2][x], 0x05040100u);
-                const uint32_t hi01 = __builtin_amdgcn_perm(rows[1][x], rows[0][x], 0x07060302u);
-                const uint32_t hi23 = __builtin_amdgcn_perm(rows[3][x], rows[2][x], 0x07060302u);
-                *(u32x2 *)&sm.vt[bi][(vch * 8 + 2 * x) * VSTR + pos] = u32x2{lo01, lo23};
-                *(u32x2 *)&sm.vt[bi][(vch * 8 + 2 * x + 1) * VSTR + pos] = u32x2{hi01, hi23};
-            }
+        for (int e = tid; e < 2 * NCH; e += 64 * C::WAVES) {
+            const bool isv = e >= NCH;
+            const int e2 = isv ? e - NCH : e;
+            const int row = e2 / (D / 16), c16 = e2 % (D / 16);
+            const u32x4 raw = *(const u32x4 *)(sm.ring + s * C::STAGEB + (isv ? KT * D : 0) + e2 * 16);
+            const int f = isv ? swz_v(row) : swz_k(row);
+            char *dst = sm.ring + NS * C::STAGEB + cb * 2 * C::TILEB + (isv ? C::TILEB : 0) + row * ROWB;
+            *(u32x4 *)(dst + ((2 * c16) ^ f) * 16) = widen8(raw[0], raw[1]);
+            *(u32x4 *)(dst + ((2 * c16 + 1) ^ f) * 16) = widen8(raw[2], raw[3]);
         }
     };
 
-    if (t0 < t1) {
-        issue_loads(t0);
-        write_stage(0, t0);
-        __syncthreads();
-    }
-    for (int kt = t0; kt < t1; ++kt) {
-        const int bi = (kt - t0) & 1;
-        if (kt + 1 < t1)
-            issue_loads(kt + 1);
+    // per-lane parts of the fragment addresses (the rest are immediates)
+    const int xk = swz_k(col);
+    int kofs[4];
+#pragma unroll
+    for (int bq = 0; bq < 4; ++bq)
+        kofs[bq] = col * ROWB + ((2 * bq + hl) ^ xk) * 16;
+    const int jv = (lane >> 2) & 3, mv = lane & 3, qd = (lane >> 4) & 1;
+    const int fv = swz_v(4 * hl + jv);
+    int vofs[2];
+#pragma unroll
+    for (int dp = 0; dp < 2; ++dp)
+        vofs[dp] = (4 * hl + jv) * ROWB + ((4 * dp + 2 * qd + (mv >> 1)) ^ fv) * 16 + (mv & 1) * 8;
 
+    auto compute_tile = [&](const char *kt_lds, const char *vt_lds, int kt) {
         const int key0 = kt * KT;
         const bool full = key0 + KT <= Ctx && key0 + KT - 1 <= P + pos0;
 #pragma unroll
@@ -268,7 +301,8 @@ __global__ __launch_bounds__(64 * PrefillCfg<D>::WAVES) void prefill_kernel(Pref
             f32x16 s = f32x16{};
 #pragma unroll
             for (int st = 0; st < ST; ++st) {
-                const u32x4 ka = *(const u32x4 *)&sm.k[bi][((kc * ST + st) * 64 + lane) * 8];
+                const u32x4 ka =
+                    *(const u32x4 *)(kt_lds + kc * 32 * ROWB + kofs[st & 3] + (st >> 2) * 128);
                 s = mfma32(ka, qb[st], s);
             }
 
@@ -325,19 +359,64 @@ __global__ __launch_bounds__(64 * PrefillCfg<D>::WAVES) void prefill_kernel(Pref
                 }
                 const u32x4 ph = u32x4{h[0], h[1], h[2], h[3]};
                 const u32x4 pl = u32x4{t[0], t[1], t[2], t[3]};
+                // V^T fragments: keys 4hl + (0..3) and 8 + 4hl + (0..3) of the step,
+                // at d = 32 dt + col
+                u32x2 vr[2 * (D / 32)];
 #pragma unroll
                 for (int dt = 0; dt < D / 32; ++dt) {
-                    const u32x4 vb =
-                        *(const u32x4 *)&sm.vt[bi][(32 * dt + col) * VSTR + 16 * ks + 8 * hl];
+                    const char *vp = vt_lds + 16 * ks * ROWB + vofs[dt & 1] + (dt >> 1) * 128;
+                    vr[2 * dt] = lds_read_tr16(vp);
+                    vr[2 * dt + 1] = lds_read_tr16(vp + 8 * ROWB);
+                }
+                lds_wait(vr);
+#pragma unroll
+                for (int dt = 0; dt < D / 32; ++dt) {
+                    const u32x4 vb = u32x4{vr[2 * dt][0], vr[2 * dt][1], vr[2 * dt + 1][0],
+                                           vr[2 * dt + 1][1]};
                     o[dt] = mfma32(ph, vb, o[dt]);
                     o[dt] = mfma32(pl, vb, o[dt]);
                 }
             }
         }
+    };
 
-        if (kt + 1 < t1)
-            write_stage(bi ^ 1, kt + 1);
-        __syncthreads();
+    if constexpr (!C::RAW) {
+        // the ring stages are the compute tiles
+        for (int u = 0; u < NS - 1 && u < nt; ++u)
+            issue_tile(t0 + u, u);
+        for (int u = 0; u < nt; ++u) {
+            const int kt = t0 + u;
+            const int ahead = nt - 1 - u < NS - 2 ? nt - 1 - u : NS - 2;
+            wait_tiles_in_flight<DPW>(ahead);
+            barrier_lds();  // tile u visible to all; stage (u - 1) % NS is free
+            if (u + NS - 1 < nt)
+                issue_tile(kt + NS - 1, (u + NS - 1) % NS);
+            const char *st_lds = sm.ring + (u % NS) * C::STAGEB;
+            compute_tile(st_lds, st_lds + C::TILEB, kt);
+        }
+    } else {
+        // raw ring -> widened double buffer, one tile ahead of the compute
+        for (int u = 0; u < NS - 1 && u < nt; ++u)
+            issue_tile(t0 + u, u);
+        if (nt > 0) {
+            wait_tiles_in_flight<DPW>(nt - 1 < NS - 2 ? nt - 1 : NS - 2);
+            barrier_lds();
+            widen_tile(0, 0);
+        }
+        for (int u = 0; u < nt; ++u) {
+            const int kt = t0 + u;
+            if (u + 1 < nt) {
+                const int ahead = nt - 2 - u < NS - 3 ? nt - 2 - u : NS - 3;
+                wait_tiles_in_flight<DPW>(ahead);  // raw tile u + 1 landed
+            }
+            barrier_lds();  // widened tile u visible; raw stage of tile u - 1 is free
+            if (u + NS - 1 < nt)
+                issue_tile(kt + NS - 1, (u + NS - 1) % NS);
+            const char *cb_lds = sm.ring + NS * C::STAGEB + (u & 1) * 2 * C::TILEB;
+            compute_tile(cb_lds, cb_lds + C::TILEB, kt);
+            if (u + 1 < nt)
+                widen_tile((u + 1) % NS, (u + 1) & 1);
+        }
     }
 
     // ---- finish: row sums, then normalise or store a partial ------------------
@@ -415,7 +494,7 @@ bool prefill_supported(int cache_dtype, int head_dim, int group)
 
 int prefill_m_tiles(int64_t total_rows, int num_q_heads, int num_kv_heads)
 {
-    const int ppt = PrefillCfg<128>::MROWS / (num_q_heads / num_kv_heads);
+    const int ppt = PrefillCfg<DT_BF16, 128>::MROWS / (num_q_heads / num_kv_heads);
     return (int)((total_rows + ppt - 1) / ppt);
 }
 
@@ -423,8 +502,8 @@ int prefill_kv_splits(int64_t total_rows, int num_q_heads)
 {
     // one work-group per CU of a 256-CU device: split the key range until the
     // (row tile, KV head) work-groups reach that count
-    const int64_t tiles = (total_rows * num_q_heads + PrefillCfg<128>::MROWS - 1) /
-                          PrefillCfg<128>::MROWS;
+    const int64_t tiles = (total_rows * num_q_heads + PrefillCfg<DT_BF16, 128>::MROWS - 1) /
+                          PrefillCfg<DT_BF16, 128>::MROWS;
     int64_t ks = tiles > 0 ? 256 / tiles : 1;
     if (ks < 1)
         ks = 1;
@@ -437,7 +516,7 @@ template <int CDT, int D>
 static hipError_t launch_prefill_t(const PrefillArgs &a, hipStream_t stream)
 {
     dim3 grid((unsigned)(a.m_tiles * a.num_kv_heads * a.kv_splits), (unsigned)a.num_reqs);
-    prefill_kernel<CDT, D><<<grid, 64 * PrefillCfg<D>::WAVES, 0, stream>>>(a);
+    prefill_kernel<CDT, D><<<grid, kPrefillThreads, 0, stream>>>(a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.kv_splits == 1)
         return e;
