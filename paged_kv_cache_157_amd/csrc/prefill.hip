@@ -36,6 +36,9 @@
 //   * Work-groups that share a (request, KV head, key slice) are numbered
 //     Hkv*splits apart, so when that product is a multiple of the XCD count
 //     they run on one XCD and its L2 serves their common K/V tiles.
+#include <type_traits>
+#include <utility>
+
 #include "pa_device.h"
 #include "pa_internal.h"
 
@@ -89,13 +92,35 @@ struct PrefillSmem {
     float ml[C::WAVES][2][32];  // [wave][max, sum][row]
 };
 
-// XOR swizzles of the 16-byte chunk index inside a K / V row of the LDS tile.
-// K rows are read 16 bytes per lane, 32 consecutive keys at one chunk: key & 7
-// spreads any 8 of them over the 8 bank groups.  V rows are read with the
-// transposing 8-byte reads: a 16-lane group touches 4 consecutive keys x 2
-// adjacent chunks, which 2 * (key & 3) + ((key >> 2) & 1) keeps apart.
-__device__ __forceinline__ int swz_k(int key) { return key & 7; }
-__device__ __forceinline__ int swz_v(int key) { return ((key & 3) << 1) | ((key >> 2) & 1); }
+// XOR swizzles of the 16-byte chunk index inside a K / V row of the LDS tile,
+// chosen so that the fragment reads below hit distinct banks whether the LDS
+// serves 128 or 256 bytes per cycle.  K rows are read 16 bytes per lane, 16
+// consecutive keys at one chunk per 256 bytes; V rows are read with the
+// transposing 8-byte reads, 4 consecutive keys x 2 (or 4) adjacent chunks per
+// 128 (or 256) bytes.
+template <int D>
+__device__ __forceinline__ int swz_k(int key)
+{
+    return D == 128 ? (key & 15) : ((key & 7) ^ ((key >> 3) & 1));
+}
+template <int D>
+__device__ __forceinline__ int swz_v(int key)
+{
+    const int j = key & 3;
+    return D == 128 ? 4 * j + 2 * (j >> 1) : 2 * j;
+}
+
+// Compile-time loop: f(std::integral_constant<int, 0>), ..., f(<N - 1>).
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, I...>)
+{
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F &&f)
+{
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 // One 16-byte chunk of bf16 (8 values) from 8 fp8 bytes, exactly.
 __device__ __forceinline__ u32x4 widen8(uint32_t w0, uint32_t w1)
@@ -110,12 +135,16 @@ __device__ __forceinline__ u32x4 widen8(uint32_t w0, uint32_t w1)
 // of a row-major tile arrives transposed.  Issued as inline assembly: the
 // compiler would otherwise wait for every outstanding global->LDS load before
 // it.  The result may only be used after lds_wait() has taken it as operand.
-__device__ __forceinline__ u32x2 lds_read_tr16(const char *p)
+template <int OFF>
+__device__ __forceinline__ u32x2 lds_read_tr16(uint32_t addr)
 {
-    const uint32_t addr = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char *)p;
     u32x2 r;
-    asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(addr) : "memory");
+    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "n"(OFF) : "memory");
     return r;
+}
+__device__ __forceinline__ uint32_t lds_addr(const void *p)
+{
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char *)p;
 }
 template <int N>
 __device__ __forceinline__ void lds_wait(u32x2 (&r)[N])
@@ -237,6 +266,18 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
     // later).  Rows past the context repeat the last context row, so every value
     // that reaches the products is finite.
     constexpr int SPR = C::SROWB / 16;  // 16-byte slots per cached row
+    // per-lane byte offset of each of this wave's instructions inside its
+    // 16-token block (the same for every tile)
+    uint32_t doff[DPW];
+#pragma unroll
+    for (int j = 0; j < DPW; ++j) {
+        const int i = w + C::WAVES * j;
+        const bool isv = i >= C::DMA_TILE / 2;
+        const int ii = isv ? i - C::DMA_TILE / 2 : i;
+        const int row = ii * C::DMA_ROWS + lane / SPR, slot = lane % SPR;
+        const int ch = C::RAW ? slot : slot ^ (isv ? swz_v<D>(row) : swz_k<D>(row));
+        doff[j] = (uint32_t)((row & 15) * tok_bytes + ch * 16);
+    }
     auto issue_tile = [&](int kt, int s) {
         int pb[4];
 #pragma unroll
@@ -253,14 +294,22 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
             const int i = w + C::WAVES * j;
             const bool isv = i >= C::DMA_TILE / 2;  // uniform
             const int ii = isv ? i - C::DMA_TILE / 2 : i;
-            const int row = ii * C::DMA_ROWS + lane / SPR;
-            const int slot = lane % SPR;
-            const int key = row < last ? row : last;
-            const int kb = key >> 4;
-            const int p = kb == 0 ? pb[0] : kb == 1 ? pb[1] : kb == 2 ? pb[2] : pb[3];
-            const int ch = C::RAW ? slot : slot ^ (isv ? swz_v(row) : swz_k(row));
-            const char *src = (isv ? vbase : kbase) + ((int64_t)p * 16 + (key & 15)) * tok_bytes + ch * 16;
-            dma16(src, sm.ring + s * C::STAGEB + (isv ? KT * C::SROWB : 0) + ii * 1024);
+            char *dst = sm.ring + s * C::STAGEB + (isv ? KT * C::SROWB : 0) + ii * 1024;
+            const char *base = isv ? vbase : kbase;
+            const int row0 = ii * C::DMA_ROWS;
+            if (row0 + C::DMA_ROWS - 1 <= last) {
+                // whole instruction inside the context: one block, scalar base
+                const int kb = row0 >> 4;
+                const int p = kb == 0 ? pb[0] : kb == 1 ? pb[1] : kb == 2 ? pb[2] : pb[3];
+                dma16(base + (int64_t)p * 16 * tok_bytes + doff[j], dst);
+            } else {
+                const int row = row0 + lane / SPR, slot = lane % SPR;
+                const int key = row < last ? row : last;
+                const int kb = key >> 4;
+                const int p = kb == 0 ? pb[0] : kb == 1 ? pb[1] : kb == 2 ? pb[2] : pb[3];
+                const int ch = C::RAW ? slot : slot ^ (isv ? swz_v<D>(row) : swz_k<D>(row));
+                dma16(base + ((int64_t)p * 16 + (key & 15)) * tok_bytes + ch * 16, dst);
+            }
         }
     };
     // fp8: widen ring stage s into compute buffer cb (bf16, swizzled rows)
@@ -272,7 +321,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
             const int e2 = isv ? e - NCH : e;
             const int row = e2 / (D / 16), c16 = e2 % (D / 16);
             const u32x4 raw = *(const u32x4 *)(sm.ring + s * C::STAGEB + (isv ? KT * D : 0) + e2 * 16);
-            const int f = isv ? swz_v(row) : swz_k(row);
+            const int f = isv ? swz_v<D>(row) : swz_k<D>(row);
             char *dst = sm.ring + NS * C::STAGEB + cb * 2 * C::TILEB + (isv ? C::TILEB : 0) + row * ROWB;
             *(u32x4 *)(dst + ((2 * c16) ^ f) * 16) = widen8(raw[0], raw[1]);
             *(u32x4 *)(dst + ((2 * c16 + 1) ^ f) * 16) = widen8(raw[2], raw[3]);
@@ -280,29 +329,35 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
     };
 
     // per-lane parts of the fragment addresses (the rest are immediates)
-    const int xk = swz_k(col);
-    int kofs[4];
+    // K: lane reads key kc*32 + col, chunk 2 st + hl
+    const int fk = swz_k<D>(col);
+    int kofs[ST];
 #pragma unroll
-    for (int bq = 0; bq < 4; ++bq)
-        kofs[bq] = col * ROWB + ((2 * bq + hl) ^ xk) * 16;
+    for (int st = 0; st < ST; ++st)
+        kofs[st] = col * ROWB + ((2 * st + hl) ^ fk) * 16;
+    // V: lane (hl, qd, j, m) of a transposing read loads key 4hl + j (+ 8, + 16 ks)
+    // at d = 32 dt + 16 qd + 4 m
     const int jv = (lane >> 2) & 3, mv = lane & 3, qd = (lane >> 4) & 1;
-    const int fv = swz_v(4 * hl + jv);
-    int vofs[2];
+    const int fv = swz_v<D>(jv);
+    int vofs[D / 32];
 #pragma unroll
-    for (int dp = 0; dp < 2; ++dp)
-        vofs[dp] = (4 * hl + jv) * ROWB + ((4 * dp + 2 * qd + (mv >> 1)) ^ fv) * 16 + (mv & 1) * 8;
+    for (int dt = 0; dt < D / 32; ++dt)
+        vofs[dt] = (4 * hl + jv) * ROWB + ((4 * dt + 2 * qd + (mv >> 1)) ^ fv) * 16 + (mv & 1) * 8;
 
     auto compute_tile = [&](const char *kt_lds, const char *vt_lds, int kt) {
         const int key0 = kt * KT;
         const bool full = key0 + KT <= Ctx && key0 + KT - 1 <= P + pos0;
+        uint32_t va[D / 32];
 #pragma unroll
-        for (int kc = 0; kc < 2; ++kc) {
+        for (int dt = 0; dt < D / 32; ++dt)
+            va[dt] = lds_addr(vt_lds) + vofs[dt];
+        static_for<2>([&](auto kc_) {
+            constexpr int kc = decltype(kc_)::value;
             // ---- S^T = K Q^T for one 32-key half ------------------------------------
             f32x16 s = f32x16{};
 #pragma unroll
             for (int st = 0; st < ST; ++st) {
-                const u32x4 ka =
-                    *(const u32x4 *)(kt_lds + kc * 32 * ROWB + kofs[st & 3] + (st >> 2) * 128);
+                const u32x4 ka = *(const u32x4 *)(kt_lds + kc * 32 * ROWB + kofs[st]);
                 s = mfma32(ka, qb[st], s);
             }
 
@@ -342,9 +397,17 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
             const float mu = mref == -INFINITY ? 0.f : mref;
 
             // ---- probabilities (bf16 head + tail) and O += P V ------------------------
-#pragma unroll
-            for (int h8 = 0; h8 < 2; ++h8) {
-                const int ks = 2 * kc + h8;  // 16-key step of the tile
+            static_for<2>([&](auto h8_) {
+                constexpr int h8 = decltype(h8_)::value;
+                constexpr int ks = 2 * kc + h8;  // 16-key step of the tile
+                // V^T fragments: keys 4hl + (0..3) and 8 + 4hl + (0..3) of the step,
+                // at d = 32 dt + col
+                u32x2 vr[2 * (D / 32)];
+                static_for<D / 32>([&](auto dt_) {
+                    constexpr int dt = decltype(dt_)::value;
+                    vr[2 * dt] = lds_read_tr16<16 * ks * ROWB>(va[dt]);
+                    vr[2 * dt + 1] = lds_read_tr16<16 * ks * ROWB + 8 * ROWB>(va[dt]);
+                });
                 float p[8];
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
@@ -359,15 +422,6 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
                 }
                 const u32x4 ph = u32x4{h[0], h[1], h[2], h[3]};
                 const u32x4 pl = u32x4{t[0], t[1], t[2], t[3]};
-                // V^T fragments: keys 4hl + (0..3) and 8 + 4hl + (0..3) of the step,
-                // at d = 32 dt + col
-                u32x2 vr[2 * (D / 32)];
-#pragma unroll
-                for (int dt = 0; dt < D / 32; ++dt) {
-                    const char *vp = vt_lds + 16 * ks * ROWB + vofs[dt & 1] + (dt >> 1) * 128;
-                    vr[2 * dt] = lds_read_tr16(vp);
-                    vr[2 * dt + 1] = lds_read_tr16(vp + 8 * ROWB);
-                }
                 lds_wait(vr);
 #pragma unroll
                 for (int dt = 0; dt < D / 32; ++dt) {
@@ -376,8 +430,8 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
                     o[dt] = mfma32(ph, vb, o[dt]);
                     o[dt] = mfma32(pl, vb, o[dt]);
                 }
-            }
-        }
+            });
+        });
     };
 
     if constexpr (!C::RAW) {
