@@ -12,15 +12,15 @@
 //     pairs of one KV head (all G heads of a position are adjacent, so one K/V
 //     tile feeds every head of the group), and one slice of the key range.
 //     Each wave holds one 32-row MFMA block.
-//   * Per 64-key tile, K and V rows are gathered through the block table.
-//     The loads for tile t+1 are issued into registers before tile t is
-//     computed and land in the other half of a double-buffered LDS tile
-//     afterwards (fp8 caches are widened to bf16 there, exactly).  K is stored
-//     in MFMA operand order: each (32-key half, 16-d step) fragment is 1 KiB
-//     that the wave reads with one contiguous 16-byte-per-lane access.  V is
-//     transposed to [d][key] so that keys are contiguous for the PV
-//     contraction, with keys of each 16-key step stored in the order the
-//     probabilities come out of the QK product.
+//   * Per 64-key tile, K and V rows are gathered through the block table
+//     straight into LDS (global_load_lds, 16 bytes per lane) through a ring of
+//     four tiles, so three tiles are in flight while one is computed; each wave
+//     counts its own loads (s_waitcnt vmcnt) and one work-group barrier per
+//     tile publishes them.  Both tiles stay row-major with XOR-swizzled
+//     16-byte chunks: K fragments (MFMA A operand, 16 bytes per lane) and V^T
+//     fragments (B operand, via the gfx950 transposing LDS read) come out
+//     without bank conflicts.  fp8 rows arrive raw and are widened to bf16
+//     (exactly) into a separate double buffer one tile ahead of the compute.
 //   * S^T = K Q^T puts one query row per lane (column of the MFMA result),
 //     so the row maximum and sum are in-lane plus one exchange between the two
 //     half-waves.  Masks are applied only on tiles that cross the causal
@@ -129,35 +129,22 @@ __device__ __forceinline__ u32x4 widen8(uint32_t w0, uint32_t w1)
                  fp8x2_to_bf16x2<true>(w1)};
 }
 
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
 // ds_read_b64_tr_b16: within each 16-lane group, lane i receives element i % 4
 // of the 4 x 16-bit values loaded by lanes i / 4, 4 + i / 4, 8 + i / 4 and
 // 12 + i / 4 (checked on gfx950 with an in-bounds probe), i.e. a 4 x 16 block
-// of a row-major tile arrives transposed.  Issued as inline assembly: the
-// compiler would otherwise wait for every outstanding global->LDS load before
-// it.  The result may only be used after lds_wait() has taken it as operand.
-template <int OFF>
-__device__ __forceinline__ u32x2 lds_read_tr16(uint32_t addr)
+// of a row-major tile arrives transposed.
+__device__ __forceinline__ u32x2 lds_read_tr16(const char *p)
 {
-    u32x2 r;
-    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "n"(OFF) : "memory");
-    return r;
+    const i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4 *)(__attribute__((address_space(3))) char *)p);
+    return __builtin_bit_cast(u32x2, r);
 }
 __device__ __forceinline__ uint32_t lds_addr(const void *p)
 {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char *)p;
 }
-template <int N>
-__device__ __forceinline__ void lds_wait(u32x2 (&r)[N])
-{
-    static_assert(N == 4 || N == 8, "operand count");
-    if constexpr (N == 4)
-        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]));
-    else
-        asm volatile("s_waitcnt lgkmcnt(0)"
-                     : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]), "+v"(r[4]), "+v"(r[5]),
-                       "+v"(r[6]), "+v"(r[7]));
-}
-
 // Work-group barrier that drains this wave's LDS operations only: the
 // global->LDS loads of later tiles stay in flight (__syncthreads would wait
 // for them too).
@@ -183,9 +170,16 @@ __device__ __forceinline__ void wait_tiles_in_flight(int n)
         wait_vm<0>();
 }
 
-__device__ __forceinline__ void dma16(const void *src, void *lds_dst)
+// 16 bytes per lane, global -> LDS at lds_dst + 16 * lane (lds_dst uniform).
+// Issued as inline assembly so that the compiler, which would otherwise wait
+// for these loads before every transposing LDS read, leaves the counting to
+// wait_vm; the LDS reads then schedule freely between the matrix products.
+__device__ __forceinline__ void dma16(const void *src, uint32_t lds_dst)
 {
-    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)lds_dst, 16, 0, 0);
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(src), "s"(lds_dst)
+                 : "memory", "m0");
 }
 
 template <int CDT, int D>
@@ -294,7 +288,8 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
             const int i = w + C::WAVES * j;
             const bool isv = i >= C::DMA_TILE / 2;  // uniform
             const int ii = isv ? i - C::DMA_TILE / 2 : i;
-            char *dst = sm.ring + s * C::STAGEB + (isv ? KT * C::SROWB : 0) + ii * 1024;
+            const uint32_t dst =
+                uniform(lds_addr(sm.ring + s * C::STAGEB + (isv ? KT * C::SROWB : 0) + ii * 1024));
             const char *base = isv ? vbase : kbase;
             const int row0 = ii * C::DMA_ROWS;
             if (row0 + C::DMA_ROWS - 1 <= last) {
@@ -344,96 +339,107 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
     for (int dt = 0; dt < D / 32; ++dt)
         vofs[dt] = (4 * hl + jv) * ROWB + ((4 * dt + 2 * qd + (mv >> 1)) ^ fv) * 16 + (mv & 1) * 8;
 
-    auto compute_tile = [&](const char *kt_lds, const char *vt_lds, int kt) {
+    // ---- S^T = K Q^T of one tile (both 32-key halves) -------------------------------
+    auto s_tile = [&](const char *kt_lds, f32x16 (&s)[2]) {
+        s[0] = f32x16{};
+        s[1] = f32x16{};
+#pragma unroll
+        for (int st = 0; st < ST; ++st)
+#pragma unroll
+            for (int kc = 0; kc < 2; ++kc) {
+                const u32x4 ka = *(const u32x4 *)(kt_lds + kc * 32 * ROWB + kofs[st]);
+                s[kc] = mfma32(ka, qb[st], s[kc]);
+            }
+    };
+    // ---- mask (diagonal / ragged tiles only), row maximum, lazy rescale --------------
+    // Raises the running maximum when the tile exceeds it by more than TAU
+    // (rescaling O and the row sum), and returns the maximum the tile's
+    // probabilities are taken against.
+    auto mask_max = [&](f32x16 (&s)[2], int kt) -> float {
         const int key0 = kt * KT;
         const bool full = key0 + KT <= Ctx && key0 + KT - 1 <= P + pos0;
-        uint32_t va[D / 32];
+        if (!full) {
 #pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt)
-            va[dt] = lds_addr(vt_lds) + vofs[dt];
-        static_for<2>([&](auto kc_) {
-            constexpr int kc = decltype(kc_)::value;
-            // ---- S^T = K Q^T for one 32-key half ------------------------------------
-            f32x16 s = f32x16{};
-#pragma unroll
-            for (int st = 0; st < ST; ++st) {
-                const u32x4 ka = *(const u32x4 *)(kt_lds + kc * 32 * ROWB + kofs[st]);
-                s = mfma32(ka, qb[st], s);
-            }
-
-            // ---- mask (diagonal / ragged tiles only), row maximum, lazy rescale ----
-            if (!full) {
+            for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     const int key = key0 + 32 * kc + 8 * (i >> 2) + 4 * hl + (i & 3);
-                    s[i] = key <= lim ? s[i] : -INFINITY;
+                    s[kc][i] = key <= lim ? s[kc][i] : -INFINITY;
                 }
-            }
-            float tm = -INFINITY;
+        }
+        float tm = -INFINITY;
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
             for (int i = 0; i < 16; ++i)
-                tm = fmaxf(tm, s[i]);
-            tm = fmaxf(tm, __shfl_xor(tm, 32)) * c;  // c > 0: scaled maximum
-            if (wave_any(tm > mref + TAU)) {
-                const float mnew = fmaxf(mref, tm);
-                const float alpha = mnew == -INFINITY ? 1.f : fast_exp2(mref - mnew);
-                lsum *= alpha;
-                mref = mnew;
-                if (hl == 0)
-                    sm.alpha[w][col] = alpha;
-                __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-                __builtin_amdgcn_wave_barrier();
+                tm = fmaxf(tm, s[kc][i]);
+        tm = fmaxf(tm, __shfl_xor(tm, 32)) * c;  // c > 0: scaled maximum
+        if (wave_any(tm > mref + TAU)) {
+            const float mnew = fmaxf(mref, tm);
+            const float alpha = mnew == -INFINITY ? 1.f : fast_exp2(mref - mnew);
+            lsum *= alpha;
+            mref = mnew;
+            if (hl == 0)
+                sm.alpha[w][col] = alpha;
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+            __builtin_amdgcn_wave_barrier();
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const float al = sm.alpha[w][8 * (i >> 2) + 4 * hl + (i & 3)];
+            for (int i = 0; i < 16; ++i) {
+                const float al = sm.alpha[w][8 * (i >> 2) + 4 * hl + (i & 3)];
 #pragma unroll
-                    for (int dt = 0; dt < D / 32; ++dt)
-                        o[dt][i] *= al;
-                }
-                __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-                __builtin_amdgcn_wave_barrier();
+                for (int dt = 0; dt < D / 32; ++dt)
+                    o[dt][i] *= al;
             }
-            // a row with no valid key yet keeps mref = -inf: its probabilities are 0
-            const float mu = mref == -INFINITY ? 0.f : mref;
-
-            // ---- probabilities (bf16 head + tail) and O += P V ------------------------
-            static_for<2>([&](auto h8_) {
-                constexpr int h8 = decltype(h8_)::value;
-                constexpr int ks = 2 * kc + h8;  // 16-key step of the tile
-                // V^T fragments: keys 4hl + (0..3) and 8 + 4hl + (0..3) of the step,
-                // at d = 32 dt + col
-                u32x2 vr[2 * (D / 32)];
-                static_for<D / 32>([&](auto dt_) {
-                    constexpr int dt = decltype(dt_)::value;
-                    vr[2 * dt] = lds_read_tr16<16 * ks * ROWB>(va[dt]);
-                    vr[2 * dt + 1] = lds_read_tr16<16 * ks * ROWB + 8 * ROWB>(va[dt]);
-                });
-                float p[8];
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+        }
+        // a row with no valid key yet keeps mref = -inf: its probabilities are 0
+        return mref == -INFINITY ? 0.f : mref;
+    };
+    // ---- probabilities (bf16 head + tail) and O += P V, four 16-key steps ----------
+    auto pv_tile = [&](const f32x16 (&s)[2], float mu, const char *vt_lds) {
+        static_for<4>([&](auto ks_) {
+            constexpr int ks = decltype(ks_)::value;
+            constexpr int kc = ks >> 1, h8 = ks & 1;
+            // V^T fragments: keys 4hl + (0..3) and 8 + 4hl + (0..3) of the step,
+            // at d = 32 dt + col
+            u32x2 vr[2 * (D / 32)];
 #pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    p[j] = fast_exp2(fmaf(s[8 * h8 + j], c, -mu));
-                    lsum += p[j];
-                }
-                uint32_t h[4], t[4];
+            for (int dt = 0; dt < D / 32; ++dt) {
+                const char *vp = vt_lds + 16 * ks * ROWB + vofs[dt];
+                vr[2 * dt] = lds_read_tr16(vp);
+                vr[2 * dt + 1] = lds_read_tr16(vp + 8 * ROWB);
+            }
+            float p[8];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    h[j] = pack_bf16(p[2 * j], p[2 * j + 1]);
-                    t[j] = pack_bf16(p[2 * j] - bf16_lo(h[j]), p[2 * j + 1] - bf16_hi(h[j]));
-                }
-                const u32x4 ph = u32x4{h[0], h[1], h[2], h[3]};
-                const u32x4 pl = u32x4{t[0], t[1], t[2], t[3]};
-                lds_wait(vr);
+            for (int j = 0; j < 8; ++j) {
+                p[j] = fast_exp2(fmaf(s[kc][8 * h8 + j], c, -mu));
+                lsum += p[j];
+            }
+            uint32_t h[4], t[4];
 #pragma unroll
-                for (int dt = 0; dt < D / 32; ++dt) {
-                    const u32x4 vb = u32x4{vr[2 * dt][0], vr[2 * dt][1], vr[2 * dt + 1][0],
-                                           vr[2 * dt + 1][1]};
-                    o[dt] = mfma32(ph, vb, o[dt]);
-                    o[dt] = mfma32(pl, vb, o[dt]);
-                }
-            });
+            for (int j = 0; j < 4; ++j) {
+                h[j] = pack_bf16(p[2 * j], p[2 * j + 1]);
+                t[j] = pack_bf16(p[2 * j] - bf16_lo(h[j]), p[2 * j + 1] - bf16_hi(h[j]));
+            }
+            const u32x4 ph = u32x4{h[0], h[1], h[2], h[3]};
+            const u32x4 pl = u32x4{t[0], t[1], t[2], t[3]};
+#pragma unroll
+            for (int dt = 0; dt < D / 32; ++dt) {
+                const u32x4 vb =
+                    u32x4{vr[2 * dt][0], vr[2 * dt][1], vr[2 * dt + 1][0], vr[2 * dt + 1][1]};
+                o[dt] = mfma32(ph, vb, o[dt]);
+                o[dt] = mfma32(pl, vb, o[dt]);
+            }
         });
     };
 
+    auto compute_tile = [&](const char *kt_lds, const char *vt_lds, int kt) {
+        f32x16 s[2];
+        s_tile(kt_lds, s);
+        const float mu = mask_max(s, kt);
+        pv_tile(s, mu, vt_lds);
+    };
     if constexpr (!C::RAW) {
         // the ring stages are the compute tiles
         for (int u = 0; u < NS - 1 && u < nt; ++u)
@@ -441,7 +447,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
         for (int u = 0; u < nt; ++u) {
             const int kt = t0 + u;
             const int ahead = nt - 1 - u < NS - 2 ? nt - 1 - u : NS - 2;
-            wait_tiles_in_flight<DPW>(ahead);
+            wait_tiles_in_flight<DPW>(ahead);  // tile u landed
             barrier_lds();  // tile u visible to all; stage (u - 1) % NS is free
             if (u + NS - 1 < nt)
                 issue_tile(kt + NS - 1, (u + NS - 1) % NS);
