@@ -620,30 +620,33 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(DecodeArgs a)
         __syncthreads();
 
         // ---- merge the waves; write the output, or a partial -----------------
-        for (int e = tid; e < G * D; e += NT) {
+        // two consecutive d of one head per thread
+        for (int e = 2 * tid; e < G * D; e += 2 * NT) {
             const int h = e / D, c = e - h * D;
             float M = -INFINITY;
 #pragma unroll
             for (int ww = 0; ww < WAVES; ++ww)
                 M = fmaxf(M, sm.msum[ww][0][h]);
-            float A = 0.f, Ls = 0.f;
+            float A0 = 0.f, A1 = 0.f, Ls = 0.f;
 #pragma unroll
             for (int ww = 0; ww < WAVES; ++ww) {
                 const float m = sm.msum[ww][0][h];
                 const float f = m == -INFINITY ? 0.f : fast_exp2(m - M);
-                A += f * sm.acc[ww][h][c];
+                A0 += f * sm.acc[ww][h][c];
+                A1 += f * sm.acc[ww][h][c + 1];
                 Ls += f * sm.msum[ww][1][h];
             }
             if (direct) {
-                a.out[((int64_t)i * Hq + g * G + h) * D + c] = A / Ls * a.v_scale;
+                float *dst = a.out + ((int64_t)i * Hq + g * G + h) * D + c;
+                const float inv = a.v_scale / Ls;
+                dst[0] = A0 * inv;
+                dst[1] = A1 * inv;
             } else {
                 // partials are written and read with device-coherent (L2-bypassing)
                 // accesses, so the hand-over below needs no cache flush
-                coherent_store(&a.ws_acc[((int64_t)slot * G + h) * D + c], A);
-                if (c == 0) {
-                    coherent_store(&a.ws_ml[((int64_t)slot * G + h) * 2 + 0], M);
-                    coherent_store(&a.ws_ml[((int64_t)slot * G + h) * 2 + 1], Ls);
-                }
+                coherent_store2(&a.ws_acc[((int64_t)slot * G + h) * D + c], A0, A1);
+                if (c == 0)
+                    coherent_store2(&a.ws_ml[((int64_t)slot * G + h) * 2], M, Ls);
             }
         }
         if (!direct) {
@@ -676,22 +679,53 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(DecodeArgs a)
                                                  __HIP_MEMORY_SCOPE_AGENT) == hi - lo;
             __syncthreads();
             if (sm.last) {
-                for (int e = tid; e < G * D; e += NT) {
+                // merge slots lo..hi: thread = 4 consecutive d of one head; the
+                // (max, sum) and accumulator loads of up to 8 slots are issued
+                // together, so a typical merge costs one memory round trip
+                const int np = hi - lo + 1;
+                for (int e = 4 * tid; e < G * D; e += 4 * NT) {
                     const int h = e / D;
-                    const float *ml = a.ws_ml + ((int64_t)lo * G + h) * 2;
-                    const float *src = a.ws_acc + (int64_t)lo * G * D + e;
-                    float M = -INFINITY;
-                    for (int s2 = 0; s2 <= hi - lo; ++s2)
-                        M = fmaxf(M, coherent_load(&ml[(int64_t)s2 * G * 2]));
-                    float num = 0.f, den = 0.f;
-#pragma unroll 4
-                    for (int s2 = 0; s2 <= hi - lo; ++s2) {
-                        const float m = coherent_load(&ml[(int64_t)s2 * G * 2]);
-                        const float f = m == -INFINITY ? 0.f : fast_exp2(m - M);
-                        num += f * coherent_load(&src[(int64_t)s2 * G * D]);
-                        den += f * coherent_load(&ml[(int64_t)s2 * G * 2 + 1]);
+                    float M = -INFINITY, den = 0.f;
+                    float num[4] = {0.f, 0.f, 0.f, 0.f};
+                    for (int s0 = 0; s0 < np; s0 += 8) {
+                        f32x2 ml[8], ac[8][2];
+#pragma unroll
+                        for (int k = 0; k < 8; ++k) {
+                            if (s0 + k < np) {
+                                const int64_t sl = lo + s0 + k;
+                                ml[k] = coherent_load2(&a.ws_ml[(sl * G + h) * 2]);
+                                ac[k][0] = coherent_load2(&a.ws_acc[sl * G * D + e]);
+                                ac[k][1] = coherent_load2(&a.ws_acc[sl * G * D + e + 2]);
+                            } else {
+                                ml[k] = f32x2{-INFINITY, 0.f};
+                                ac[k][0] = ac[k][1] = f32x2{0.f, 0.f};
+                            }
+                        }
+                        float Mb = M;
+#pragma unroll
+                        for (int k = 0; k < 8; ++k)
+                            Mb = fmaxf(Mb, ml[k][0]);
+                        const float fo = M == -INFINITY ? 0.f : fast_exp2(M - Mb);
+                        den *= fo;
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            num[j] *= fo;
+#pragma unroll
+                        for (int k = 0; k < 8; ++k) {
+                            const float f = ml[k][0] == -INFINITY ? 0.f : fast_exp2(ml[k][0] - Mb);
+                            den += f * ml[k][1];
+                            num[0] += f * ac[k][0][0];
+                            num[1] += f * ac[k][0][1];
+                            num[2] += f * ac[k][1][0];
+                            num[3] += f * ac[k][1][1];
+                        }
+                        M = Mb;
                     }
-                    a.out[((int64_t)i * Hq + g * G) * D + e] = num / den * a.v_scale;
+                    const float inv = a.v_scale / den;
+                    float *dst = a.out + ((int64_t)i * Hq + g * G) * D + e;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        dst[j] = num[j] * inv;
                 }
                 if (tid == 0)
                     a.ws_count[pair] = 0;  // leave the counter at zero for the next call
