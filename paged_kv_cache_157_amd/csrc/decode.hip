@@ -144,11 +144,15 @@ template <int CDT, int D, int G, int NSTAGE, int WAVES>
 struct DecodeSmem {
     using C = DecodeCfg<CDT, D, G>;
     static constexpr int KB = 16 * D * C::EB;  // bytes of one block of one KV head (K or V)
-    union {
-        // per-wave ring of NSTAGE blocks, K then V, filled by global->LDS DMA
-        uint8_t ring[WAVES][NSTAGE][2 * KB];
-        float acc[WAVES][G][D];  // per-wave accumulators at a segment end
-    };
+    // bytes of the q rows of one (sequence, KV head): G heads x D (fp32 q with
+    // an fp32 cache, else bf16), rounded up to whole 1 KiB DMA instructions
+    static constexpr int QB = G * D * (CDT == DT_F32 ? 4 : 2);
+    static constexpr int QBR = (QB + 1023) / 1024 * 1024;
+    // per-wave ring of NSTAGE blocks, K then V, filled by global->LDS DMA; at a
+    // segment end the last stage holds the wave's accumulators (G x D fp32)
+    __attribute__((aligned(16))) uint8_t ring[WAVES][NSTAGE][2 * KB];
+    // q of the current and of the next segment (double buffer)
+    __attribute__((aligned(16))) uint8_t qbuf[2][QBR];
     float p[WAVES][16][8];       // probabilities of the current block
     float bmax[WAVES][4][8];     // row maxima (rescale path)
     float msum[WAVES][2][8];     // per-wave running max and sum
@@ -300,88 +304,129 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(DecodeArgs a)
     uint8_t *my_ring = &sm.ring[w][0][0];
 
     const auto lens_s = scalar_view(a.context_lens);
-    while (item < a1) {
-        // ---- next segment (every value here is wave-uniform) ---------------
-        int L = lens_s[i];
-        int n_i = items_of(L);
-        while (n_i == 0) {  // cannot happen for the first segment; skip empties
-            ++i;
-            L = lens_s[i];
-            n_i = items_of(L);
+    static_assert(G * D * 4 <= 2 * KB && NSTAGE >= 2, "accumulators fit in one ring stage");
+    constexpr int QEB = CDT == DT_F32 ? 4 : 2;  // bytes per q element
+
+    // A segment: the items of one (sequence, KV head) inside [item, a1).  Every
+    // value is wave-uniform.  Sequences without items are skipped (advances si).
+    struct Seg {
+        int L, n_i, g, x, seg_items, b0, b1, slot;
+    };
+    auto describe = [&](long long it, int &si, long long sbase) -> Seg {
+        Seg d;
+        int L = lens_s[si];
+        int n = items_of(L);
+        while (n == 0) {  // cannot happen for the first segment; skip empties
+            ++si;
+            L = lens_s[si];
+            n = items_of(L);
         }
-        L = uniform(L > maxB * 16 ? maxB * 16 : L);
-        n_i = uniform(n_i);
-        const long long rel = item - base_i;
-        const int g = uniform((int)(rel / n_i));
-        const int x = uniform((int)(rel - (long long)g * n_i));
-        const int nblk = (L + 15) >> 4;
-        int seg_items, b0, b1, slot;
+        d.L = uniform(L > maxB * 16 ? maxB * 16 : L);
+        d.n_i = uniform(n);
+        const long long rel = it - sbase;
+        d.g = uniform((int)(rel / d.n_i));
+        d.x = uniform((int)(rel - (long long)d.g * d.n_i));
+        const int nblk = (d.L + 15) >> 4;
         if (PB > 0) {
-            seg_items = 1;
-            b0 = x * PB;
-            b1 = b0 + PB < nblk ? b0 + PB : nblk;
-            slot = (int)item;
+            d.seg_items = 1;
+            d.b0 = d.x * PB;
+            d.b1 = d.b0 + PB < nblk ? d.b0 + PB : nblk;
+            d.slot = (int)it;
         } else {
-            const long long left = a1 - item;
-            seg_items = (int)((long long)(n_i - x) < left ? (n_i - x) : left);
-            b0 = x;
-            b1 = x + seg_items;
+            const long long left = a1 - it;
+            d.seg_items = (int)((long long)(d.n_i - d.x) < left ? (d.n_i - d.x) : left);
+            d.b0 = d.x;
+            d.b1 = d.x + d.seg_items;
             // rank of this work-group among those with a non-empty range: with at
             // least as many items as work-groups every range is non-empty (rank =
             // blockIdx.x); with fewer, each non-empty range holds one item (rank =
             // a0).  Ranks keep the partial slots of one (sequence, head) contiguous.
-            slot = (int)(a0 < (long long)blockIdx.x ? a0 : (long long)blockIdx.x) + i * Hkv + g;
+            d.slot = (int)(a0 < (long long)blockIdx.x ? a0 : (long long)blockIdx.x) + si * Hkv + d.g;
         }
-        b0 = uniform(b0);
-        b1 = uniform(b1);
+        d.b0 = uniform(d.b0);
+        d.b1 = uniform(d.b1);
+        return d;
+    };
+    // q rows of (sequence si, KV head gg) -> qbuf[buf], by wave 0
+    auto issue_q = [&](int si, int gg, int buf) {
+        if (w == 0) {
+            const char *src = (const char *)a.q + ((int64_t)si * Hq + gg * G) * D * QEB;
+#pragma unroll
+            for (int k = 0; k < SM::QBR / 1024; ++k) {
+                const int off = k * 1024 + lane * 16;
+                dma16(src + (off < SM::QB ? off : 0), &sm.qbuf[buf][k * 1024]);
+            }
+        }
+    };
+    // first block of this wave in a segment -> ring stage 0
+    auto issue_first = [&](int si, const Seg &d) -> bool {
+        if (d.b0 + w >= d.b1)
+            return false;
+        const int pb0 = uniform(scalar_view(a.block_tables + (int64_t)si * maxB)[d.b0 + w]);
+        const unsigned pb = (unsigned)pb0 < nblocks_pool ? (unsigned)pb0 : 0u;
+        const char *kp = (const char *)a.k_cache + (int64_t)d.g * D * C::EB + (int64_t)pb * blk_bytes;
+        const char *vp = (const char *)a.v_cache + (int64_t)d.g * D * C::EB + (int64_t)pb * blk_bytes;
+#pragma unroll
+        for (int j = 0; j < ROUNDS; ++j)
+#pragma unroll
+            for (int c = 0; c < CPL; ++c)
+                dma16(kp + (size_t)koff[j][c], my_ring + (j * CPL + c) * 1024);
+#pragma unroll
+        for (int v = 0; v < VPASS; ++v)
+            dma16(vp + (size_t)voff[v], my_ring + KB + v * 1024);
+        return true;
+    };
+
+    Seg sg = describe(item, i, base_i);
+    issue_q(i, sg.g, 0);
+    wait_vm<0>();
+    __syncthreads();
+    int qbi = 0;        // q buffer of the current segment
+    bool pre0 = false;  // this wave's first block of the segment is already in stage 0
+    for (;;) {
+        const int L = sg.L, n_i = sg.n_i, g = sg.g, x = sg.x, seg_items = sg.seg_items;
+        const int b0 = sg.b0, b1 = sg.b1, slot = sg.slot;
         const bool first = x == 0;
         const bool last = x + seg_items == n_i;
         const bool direct = first && last;
+        // the following segment: its q is fetched now, during this one
+        const long long item_n = item + seg_items;
+        const bool has_next = item_n < a1;
+        int i_n = i;
+        long long base_n = base_i;
+        if (last && g == Hkv - 1) {
+            base_n += (long long)n_i * Hkv;
+            ++i_n;
+        }
+        Seg nx = sg;
+        if (has_next) {
+            nx = describe(item_n, i_n, base_n);
+            issue_q(i_n, nx.g, qbi ^ 1);
+        }
 
         // ---- q for this (sequence, KV head), slot s = head (s ^ lane_m) ---
         uint32_t qr[GP][CPL][QW];
-        {
-            const int hq0 = g * G;
 #pragma unroll
-            for (int s = 0; s < GP; ++s) {
-                const int h = s ^ lane_m;
+        for (int s = 0; s < GP; ++s) {
+            const int h = s ^ lane_m;
 #pragma unroll
-                for (int c = 0; c < CPL; ++c) {
-                    const int chunk = gl + c * LPT;
-                    if (h < G) {
-                        const char *qp = (const char *)a.q;
-                        if constexpr (CDT == DT_F32) {
-                            const u32x4 t = *(const u32x4 *)(qp + (((int64_t)i * Hq + hq0 + h) * D +
-                                                                   chunk * E) * 4);
+            for (int c = 0; c < CPL; ++c) {
+                const int chunk = gl + c * LPT;
+                if (h < G) {
+                    const u32x4 *t = (const u32x4 *)&sm.qbuf[qbi][(h * D + chunk * E) * QEB];
 #pragma unroll
-                            for (int k = 0; k < 4; ++k)
-                                qr[s][c][k] = t[k];
-                        } else {
-                            const u32x4 *t = (const u32x4 *)(qp + (((int64_t)i * Hq + hq0 + h) * D +
-                                                                   chunk * E) * 2);
+                    for (int k = 0; k < QW / 4; ++k) {
+                        const u32x4 u = t[k];
 #pragma unroll
-                            for (int k = 0; k < QW / 4; ++k) {
-                                const u32x4 u = t[k];
-#pragma unroll
-                                for (int e = 0; e < 4; ++e)
-                                    qr[s][c][4 * k + e] = u[e];
-                            }
-                        }
-                    } else {
-#pragma unroll
-                        for (int k = 0; k < QW; ++k)
-                            qr[s][c][k] = 0;
+                        for (int e = 0; e < 4; ++e)
+                            qr[s][c][4 * k + e] = u[e];
                     }
-                }
-            }
-            // q must land before the ring's DMA loads are queued behind it
-#pragma unroll
-            for (int s = 0; s < GP; ++s)
-#pragma unroll
-                for (int c = 0; c < CPL; ++c)
+                } else {
 #pragma unroll
                     for (int k = 0; k < QW; ++k)
-                        settle(qr[s][c][k]);
+                        qr[s][c][k] = 0;
+                }
+            }
         }
 
         // ---- per-wave streaming softmax over blocks b0+w, b0+w+WAVES, ... ---
@@ -421,7 +466,7 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(DecodeArgs a)
         // prologue: NSTAGE - 1 blocks in flight
 #pragma unroll
         for (int t = 0; t < NSTAGE - 1; ++t)
-            if (t < nb_w)
+            if (t < nb_w && !(t == 0 && pre0))
                 issue(t, uniform(table[b0 + w + WAVES * t]));
         int pb_ahead = NSTAGE - 1 < nb_w ? uniform(table[b0 + w + WAVES * (NSTAGE - 1)]) : 0;
 
@@ -582,6 +627,17 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(DecodeArgs a)
             __builtin_amdgcn_wave_barrier();
         }
 
+        // ---- the following segment's first block goes out now, so its load
+        // overlaps this segment's hand-over below (stage 0 is free: this
+        // wave's blocks are consumed; the accumulators use the last stage)
+        pre0 = has_next && issue_first(i_n, nx);
+        if (w == 0) {  // the next segment's q (issued before any ring load) has landed
+            if (pre0)
+                wait_vm<LPB>();
+            else
+                wait_vm<0>();
+        }
+
         // ---- wave totals -> LDS --------------------------------------------
         // sum over rows and over the lanes of a row that hold other tokens
         float ls = lane_owner ? lsum : 0.f;
@@ -602,13 +658,13 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(DecodeArgs a)
                 }
                 acc[h][e] = t;
             }
-        __syncthreads();  // every wave is done with its ring (aliased below)
         if (lane < NC) {
+            float *accw = (float *)&sm.ring[w][NSTAGE - 1][0];
 #pragma unroll
             for (int h = 0; h < G; ++h)
 #pragma unroll
                 for (int e = 0; e < E; ++e)
-                    sm.acc[w][h][lane * E + e] = acc[h][e];
+                    accw[h * D + lane * E + e] = acc[h][e];
         }
         if (lane < 16 && tr == 0 && lane_owner)
             sm.msum[w][1][lane_m] = ls;
@@ -632,8 +688,9 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(DecodeArgs a)
             for (int ww = 0; ww < WAVES; ++ww) {
                 const float m = sm.msum[ww][0][h];
                 const float f = m == -INFINITY ? 0.f : fast_exp2(m - M);
-                A0 += f * sm.acc[ww][h][c];
-                A1 += f * sm.acc[ww][h][c + 1];
+                const float *accw = (const float *)&sm.ring[ww][NSTAGE - 1][0];
+                A0 += f * accw[h * D + c];
+                A1 += f * accw[h * D + c + 1];
                 Ls += f * sm.msum[ww][1][h];
             }
             if (direct) {
@@ -734,11 +791,13 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(DecodeArgs a)
         __syncthreads();
 
         // ---- advance ----------------------------------------------------------
-        item += seg_items;
-        if (last && g == Hkv - 1) {
-            base_i += (long long)n_i * Hkv;
-            ++i;
-        }
+        if (!has_next)
+            break;
+        item = item_n;
+        i = i_n;
+        base_i = base_n;
+        sg = nx;
+        qbi ^= 1;
     }
 }
 
