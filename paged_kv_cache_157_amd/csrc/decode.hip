@@ -377,6 +377,27 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(DecodeArgs a)
         return true;
     };
 
+    // Issue priority follows this wave's remaining work (3 at the start, 0 near
+    // the end): when two work-groups share a CU, the one that has fallen behind
+    // gets the instruction slots, instead of the older one by default, so both
+    // finish together.  Only the order of issue changes, never the arithmetic.
+    const int exp_w = (int)((a1 - a0 + WAVES - 1) / WAVES);  // this wave's share, blocks
+    int done_w = 0, cur_prio = -1;
+    auto update_priority = [&]() {
+        const int pr = 3 - min(3, (4 * done_w) / (exp_w > 0 ? exp_w : 1));
+        if (pr != cur_prio) {
+            cur_prio = pr;
+            if (pr == 3)
+                __builtin_amdgcn_s_setprio(3);
+            else if (pr == 2)
+                __builtin_amdgcn_s_setprio(2);
+            else if (pr == 1)
+                __builtin_amdgcn_s_setprio(1);
+            else
+                __builtin_amdgcn_s_setprio(0);
+        }
+    };
+
     Seg sg = describe(item, i, base_i);
     issue_q(i, sg.g, 0);
     wait_vm<0>();
@@ -471,6 +492,8 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(DecodeArgs a)
         int pb_ahead = NSTAGE - 1 < nb_w ? uniform(table[b0 + w + WAVES * (NSTAGE - 1)]) : 0;
 
         for (int t = 0; t < nb_w; ++t) {
+            update_priority();
+            ++done_w;
             const int b = b0 + w + WAVES * t;
             // keep NSTAGE - 1 blocks ahead in flight; fetch the next table entry early
             if (t + NSTAGE - 1 < nb_w) {
