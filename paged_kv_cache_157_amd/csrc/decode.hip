@@ -40,7 +40,7 @@
 namespace pa {
 
 #ifndef DECODE_STAGES
-#define DECODE_STAGES 2  // blocks of K/V in a wave's LDS ring (NSTAGE - 1 in flight)
+#define DECODE_STAGES 2  // blocks of K/V in a wave's LDS ring (the loop is written for 2)
 #endif
 #ifndef DECODE_WAVES
 #define DECODE_WAVES 4   // waves per work-group; they split a segment's blocks
@@ -169,20 +169,6 @@ __device__ __forceinline__ void wait_vm()
 {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
-template <int LPB, int NSTAGE>
-__device__ __forceinline__ void wait_blocks_after(int n)
-{
-    // n = blocks whose loads were issued after the one about to be read
-    if constexpr (NSTAGE >= 4) {
-        if (n >= 3) { wait_vm<3 * LPB>(); return; }
-    }
-    if constexpr (NSTAGE >= 3) {
-        if (n >= 2) { wait_vm<2 * LPB>(); return; }
-    }
-    if (n >= 1) { wait_vm<LPB>(); return; }
-    wait_vm<0>();
-}
-
 __device__ __forceinline__ void dma16(const void *src, void *lds_dst)
 {
     __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)lds_dst, 16, 0, 0);
@@ -304,7 +290,7 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(DecodeArgs a)
     uint8_t *my_ring = &sm.ring[w][0][0];
 
     const auto lens_s = scalar_view(a.context_lens);
-    static_assert(G * D * 4 <= 2 * KB && NSTAGE >= 2, "accumulators fit in one ring stage");
+    static_assert(G * D * 4 <= 2 * KB && NSTAGE == 2, "two ring stages; accumulators fit in one");
     constexpr int QEB = CDT == DT_F32 ? 4 : 2;  // bytes per q element
 
     // A segment: the items of one (sequence, KV head) inside [item, a1).  Every
@@ -470,40 +456,52 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(DecodeArgs a)
 
         // blocks of this wave: b0 + w + WAVES*t, t < nb_w
         const int nb_w = b1 - b0 - w > 0 ? (b1 - b0 - w + WAVES - 1) / WAVES : 0;
-        auto issue = [&](int t, int pb) {
+        // Two ring stages per wave.  K of block t + 2 is loaded into the K half
+        // of block t's stage as soon as QK(t) is done, V of block t + 2 into the
+        // V half once PV(t) is done, so about 1.5 blocks stay in flight per wave.
+        constexpr int NK = ROUNDS * CPL, NV = VPASS;  // DMA instructions per block (K, V)
+        auto issue_k = [&](int t, int pb) {
             pb = (unsigned)pb < nblocks_pool ? pb : 0;
             const char *kp = kbase + (int64_t)pb * blk_bytes;
-            const char *vp = vbase + (int64_t)pb * blk_bytes;
-            uint8_t *st = my_ring + (t % NSTAGE) * 2 * KB;
+            uint8_t *st = my_ring + (t & 1) * 2 * KB;
 #pragma unroll
             for (int j = 0; j < ROUNDS; ++j)
 #pragma unroll
                 for (int c = 0; c < CPL; ++c)
                     dma16(kp + (size_t)koff[j][c], st + (j * CPL + c) * 1024);
+        };
+        auto issue_v = [&](int t, int pb) {
+            pb = (unsigned)pb < nblocks_pool ? pb : 0;
+            const char *vp = vbase + (int64_t)pb * blk_bytes;
+            uint8_t *st = my_ring + (t & 1) * 2 * KB;
 #pragma unroll
             for (int v = 0; v < VPASS; ++v)
                 dma16(vp + (size_t)voff[v], st + KB + v * 1024);
         };
-        // prologue: NSTAGE - 1 blocks in flight
-#pragma unroll
-        for (int t = 0; t < NSTAGE - 1; ++t)
-            if (t < nb_w && !(t == 0 && pre0))
-                issue(t, uniform(table[b0 + w + WAVES * t]));
-        int pb_ahead = NSTAGE - 1 < nb_w ? uniform(table[b0 + w + WAVES * (NSTAGE - 1)]) : 0;
+        // prologue: blocks 0 and 1 in flight (block 0 may already be on its way)
+        if (nb_w > 0 && !pre0) {
+            const int p0 = uniform(table[b0 + w]);
+            issue_k(0, p0);
+            issue_v(0, p0);
+        }
+        if (nb_w > 1) {
+            const int p1 = uniform(table[b0 + w + WAVES]);
+            issue_k(1, p1);
+            issue_v(1, p1);
+        }
 
         for (int t = 0; t < nb_w; ++t) {
             update_priority();
             ++done_w;
             const int b = b0 + w + WAVES * t;
-            // keep NSTAGE - 1 blocks ahead in flight; fetch the next table entry early
-            if (t + NSTAGE - 1 < nb_w) {
-                issue(t + NSTAGE - 1, pb_ahead);
-                if (t + NSTAGE < nb_w)
-                    pb_ahead = uniform(table[b + WAVES * NSTAGE]);
-            }
-            const int after = nb_w - 1 - t < NSTAGE - 1 ? nb_w - 1 - t : NSTAGE - 1;
-            wait_blocks_after<LPB, NSTAGE>(after);
-            const uint8_t *st = my_ring + (t % NSTAGE) * 2 * KB + lane * 16;
+            const bool more1 = t + 1 < nb_w, more2 = t + 2 < nb_w;  // uniform
+            const int pb2 = more2 ? uniform(table[b + 2 * WAVES]) : 0;
+            // K(t); issued after it and possibly in flight: V(t), K(t+1), V(t+1)
+            if (more1)
+                wait_vm<NV + NK + NV>();
+            else
+                wait_vm<NV>();
+            const uint8_t *st = my_ring + (t & 1) * 2 * KB + lane * 16;
 
             // -- scores of this lane's token(s) for head lane_m ------------
             const int tbase = b * 16;
@@ -547,6 +545,12 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(DecodeArgs a)
                 const float s2 = reduce_scatter<LPT, GP>(xs) * a.qk_scale;
                 const int tt = tbase + row_token<LPT>(row, tr + j * C::TRN);
                 sc[j] = tt < L ? s2 : -INFINITY;
+            }
+
+            // K(t) is consumed: its half of the stage takes K(t+2)
+            if (more2) {
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                issue_k(t + 2, pb2);
             }
 
             // -- block maximum of the row for head lane_m ------------------
@@ -599,6 +603,13 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(DecodeArgs a)
             __builtin_amdgcn_wave_barrier();
 
             // -- PV ----------------------------------------------------------
+            // V(t); issued after it and possibly in flight: K(t+1), V(t+1), K(t+2)
+            if (more2)
+                wait_vm<NK + NV + NK>();
+            else if (more1)
+                wait_vm<NK + NV>();
+            else
+                wait_vm<0>();
             u32x4 vrow[VPASS];
 #pragma unroll
             for (int v = 0; v < VPASS; ++v)
@@ -645,6 +656,11 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(DecodeArgs a)
 #pragma unroll
                     for (int e = 0; e < E; ++e)
                         acc[h][e] = fmaf(pr[h], ve[e], acc[h][e]);
+            }
+            // V(t) is consumed: its half of the stage takes V(t+2)
+            if (more2) {
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                issue_v(t + 2, pb2);
             }
             __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
             __builtin_amdgcn_wave_barrier();
