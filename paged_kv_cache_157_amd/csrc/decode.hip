@@ -366,11 +366,16 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(DecodeArgs a)
     // Issue priority follows this wave's remaining work (3 at the start, 0 near
     // the end): when two work-groups share a CU, the one that has fallen behind
     // gets the instruction slots, instead of the older one by default, so both
-    // finish together.  Only the order of issue changes, never the arithmetic.
+    // finish together.  The persistent grid fills every CU's first slot with
+    // work-groups [0, grid/2) before the second; the later ones lower their
+    // priority half a step later, which cancels the age tie-break at equal
+    // progress.  Only the order of issue changes, never the arithmetic.
     const int exp_w = (int)((a1 - a0 + WAVES - 1) / WAVES);  // this wave's share, blocks
+    const int ew = exp_w > 0 ? exp_w : 1;
+    const int lag = blockIdx.x >= gridDim.x / 2 ? ew / 2 : 0;
     int done_w = 0, cur_prio = -1;
     auto update_priority = [&]() {
-        const int pr = 3 - min(3, (4 * done_w) / (exp_w > 0 ? exp_w : 1));
+        const int pr = 3 - min(3, max(0, 4 * done_w - lag) / ew);
         if (pr != cur_prio) {
             cur_prio = pr;
             if (pr == 3)
