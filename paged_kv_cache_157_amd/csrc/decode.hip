@@ -131,6 +131,15 @@ __device__ __forceinline__ bool mask_owner(int lane)
         return (lane & 3) == 0;
 }
 
+// Sum over the 64 lanes of a wave.
+__device__ __forceinline__ long long wave_sum64(long long v)
+{
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1)
+        v += __shfl_xor(v, d);
+    return v;
+}
+
 // Sum of a value over the 64 lanes that share a "column" pattern: lanes that
 // differ only in the row (bits 4-5) and in the bits selected by the pattern.
 __device__ __forceinline__ float sum_rows(float v)
@@ -156,7 +165,7 @@ struct DecodeSmem {
     float p[WAVES][16][8];       // probabilities of the current block
     float bmax[WAVES][4][8];     // row maxima (rescale path)
     float msum[WAVES][2][8];     // per-wave running max and sum
-    long long scan[64 * WAVES];
+    long long total;  // item count of the call (start-up scan)
     int last;
     int seg_i;
     long long seg_base;
@@ -201,19 +210,50 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(DecodeArgs a)
         return PB > 0 ? (nb + PB - 1) / PB : nb;
     };
 
-    // ---- total item count and this work-group's range --------------------
-    long long part = 0;
-    for (int i = tid; i < S; i += NT)
-        part += items_of(a.context_lens[i]);
-    sm.scan[tid] = part;
-    __syncthreads();
-    for (int s = NT / 2; s > 0; s >>= 1) {
-        if (tid < s)
-            sm.scan[tid] += sm.scan[tid + s];
-        __syncthreads();
+    // ---- total item count and the sequence holding this work-group's first
+    // item: wave 0 scans the lengths 64 at a time with shuffles (no work-group
+    // barrier inside); the other waves wait at the barrier below.
+    if (w == 0) {
+        const long long v0 = lane < S ? (long long)items_of(a.context_lens[lane]) : 0;
+        long long cnt = wave_sum64(v0);
+        for (int base = 64; base < S; base += 64) {
+            const int s2 = base + lane;
+            cnt += wave_sum64(s2 < S ? (long long)items_of(a.context_lens[s2]) : 0);
+        }
+        const long long tot = cnt * Hkv;
+        const long long x0 = tot * blockIdx.x / gridDim.x;
+        int found = -1;
+        long long fbase = 0, carry = 0;
+        for (int base = 0; base < S; base += 64) {
+            const int s2 = base + lane;
+            const long long v =
+                (base == 0 ? v0 : s2 < S ? (long long)items_of(a.context_lens[s2]) : 0) * Hkv;
+            long long incl = v;
+#pragma unroll
+            for (int d = 1; d < 64; d <<= 1) {
+                const long long t = __shfl_up(incl, d);
+                if (lane >= d)
+                    incl += t;
+            }
+            const long long excl = incl - v;
+            const unsigned long long m =
+                __builtin_amdgcn_ballot_w64(v > 0 && carry + excl <= x0 && x0 < carry + incl);
+            if (m) {
+                const int l = __builtin_ctzll(m);
+                found = base + l;
+                fbase = carry + __shfl(excl, l);
+                break;
+            }
+            carry += __shfl(incl, 63);
+        }
+        if (lane == 0) {
+            sm.total = tot;
+            sm.seg_i = found;
+            sm.seg_base = fbase;
+        }
     }
-    const long long total = uniform64(sm.scan[0]) * Hkv;
     __syncthreads();
+    const long long total = uniform64(sm.total);
     if (blockIdx.x == 0) {  // sequences with no tokens get a zero output row
         for (int i = tid; i < S; i += NT)
             if (a.context_lens[i] <= 0)
@@ -224,34 +264,6 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(DecodeArgs a)
     const long long a1 = total * (blockIdx.x + 1) / gridDim.x;
     if (a0 >= a1)
         return;
-
-    // ---- locate the sequence holding item a0 (chunked inclusive scan) ----
-    if (tid == 0)
-        sm.seg_i = -1;
-    long long carry = 0;
-    for (int base = 0; base < S; base += NT) {
-        const int i = base + tid;
-        const long long v = i < S ? (long long)items_of(a.context_lens[i]) * Hkv : 0;
-        __syncthreads();
-        sm.scan[tid] = v;
-        __syncthreads();
-        for (int s = 1; s < NT; s <<= 1) {
-            long long t = tid >= s ? sm.scan[tid - s] : 0;
-            __syncthreads();
-            sm.scan[tid] += t;
-            __syncthreads();
-        }
-        const long long incl = carry + sm.scan[tid];
-        const long long excl = incl - v;
-        if (i < S && v > 0 && excl <= a0 && a0 < incl) {
-            sm.seg_i = i;
-            sm.seg_base = excl;
-        }
-        carry += sm.scan[NT - 1];
-        __syncthreads();
-        if (sm.seg_i >= 0)
-            break;
-    }
     int i = uniform(sm.seg_i);
     if (i < 0)  // unreachable while a0 < total; keeps every index in range
         return;
