@@ -135,10 +135,10 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 // of the 4 x 16-bit values loaded by lanes i / 4, 4 + i / 4, 8 + i / 4 and
 // 12 + i / 4 (checked on gfx950 with an in-bounds probe), i.e. a 4 x 16 block
 // of a row-major tile arrives transposed.
-__device__ __forceinline__ u32x2 lds_read_tr16(const char *p)
+typedef __attribute__((address_space(3))) char lds_char;
+__device__ __forceinline__ u32x2 lds_read_tr16(lds_char *p)
 {
-    const i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) i16x4 *)(__attribute__((address_space(3))) char *)p);
+    const i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4 *)p);
     return __builtin_bit_cast(u32x2, r);
 }
 __device__ __forceinline__ uint32_t lds_addr(const void *p)
@@ -403,10 +403,12 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
             constexpr int kc = ks >> 1, h8 = ks & 1;
             // V^T fragments: keys 4hl + (0..3) and 8 + 4hl + (0..3) of the step,
             // at d = 32 dt + col
+            // (the LDS-space base keeps the constant offsets in the instructions)
+            lds_char *vt3 = (lds_char *)vt_lds;
             u32x2 vr[2 * (D / 32)];
 #pragma unroll
             for (int dt = 0; dt < D / 32; ++dt) {
-                const char *vp = vt_lds + 16 * ks * ROWB + vofs[dt];
+                lds_char *vp = vt3 + vofs[dt] + 16 * ks * ROWB;
                 vr[2 * dt] = lds_read_tr16(vp);
                 vr[2 * dt + 1] = lds_read_tr16(vp + 8 * ROWB);
             }
