@@ -178,6 +178,11 @@ __device__ __forceinline__ void wait_vm()
 {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
+// Work-group barrier for LDS data only: every wave's LDS accesses have
+// completed (lgkmcnt), global loads may stay in flight.  Where a hand-over
+// needs global memory complete, the code waits for it explicitly first.
+__device__ __forceinline__ void barrier_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 __device__ __forceinline__ void dma16(const void *src, void *lds_dst)
 {
     __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)lds_dst, 16, 0, 0);
@@ -252,7 +257,7 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(DecodeArgs a)
             sm.seg_base = fbase;
         }
     }
-    __syncthreads();
+    barrier_lds();
     const long long total = uniform64(sm.total);
     if (blockIdx.x == 0) {  // sequences with no tokens get a zero output row
         for (int i = tid; i < S; i += NT)
@@ -401,12 +406,19 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(DecodeArgs a)
         }
     };
 
+    // the first segment's q and each wave's first block go out together;
+    // wave 0 then waits for q only
     Seg sg = describe(item, i, base_i);
     issue_q(i, sg.g, 0);
-    wait_vm<0>();
-    __syncthreads();
-    int qbi = 0;        // q buffer of the current segment
-    bool pre0 = false;  // this wave's first block of the segment is already in stage 0
+    bool pre0 = issue_first(i, sg);  // this wave's first block of the segment is already in stage 0
+    if (w == 0) {
+        if (pre0)
+            wait_vm<LPB>();
+        else
+            wait_vm<0>();
+    }
+    barrier_lds();
+    int qbi = 0;  // q buffer of the current segment
     for (;;) {
         const int L = sg.L, n_i = sg.n_i, g = sg.g, x = sg.x, seg_items = sg.seg_items;
         const int b0 = sg.b0, b1 = sg.b1, slot = sg.slot;
@@ -729,7 +741,7 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(DecodeArgs a)
             for (int h = 0; h < G; ++h)
                 sm.msum[w][0][h] = mref[h];
         }
-        __syncthreads();
+        barrier_lds();
 
         // ---- merge the waves; write the output, or a partial -----------------
         // two consecutive d of one head per thread
@@ -786,11 +798,11 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(DecodeArgs a)
                 hi = (int)r_last + pair;
             }
             wait_vm<0>();
-            __syncthreads();
+            barrier_lds();
             if (tid == 0)
                 sm.last = __hip_atomic_fetch_add(&a.ws_count[pair], 1, __ATOMIC_RELAXED,
                                                  __HIP_MEMORY_SCOPE_AGENT) == hi - lo;
-            __syncthreads();
+            barrier_lds();
             if (sm.last) {
                 // merge slots lo..hi: thread = 4 consecutive d of one head; the
                 // (max, sum) and accumulator loads of up to 8 slots are issued
@@ -844,7 +856,7 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(DecodeArgs a)
                     a.ws_count[pair] = 0;  // leave the counter at zero for the next call
             }
         }
-        __syncthreads();
+        barrier_lds();
 
         // ---- advance ----------------------------------------------------------
         if (!has_next)
