@@ -142,11 +142,29 @@ __device__ __forceinline__ long long wave_sum64(long long v)
 
 // Sum of a value over the 64 lanes that share a "column" pattern: lanes that
 // differ only in the row (bits 4-5) and in the bits selected by the pattern.
+// gfx950's lane swaps exchange the wave halves (rows 0-1 <-> 2-3) and
+// neighbouring rows in registers: swapping a value with itself leaves
+// {v(l), v(l ^ 32)} (then {v(l), v(l ^ 16)}) in the two results of every
+// lane l.
 __device__ __forceinline__ float sum_rows(float v)
 {
-    v += __shfl_xor(v, 32);
-    v += __shfl_xor(v, 16);
-    return v;
+    const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(h[0]) + __uint_as_float(h[1]);
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave (32-bit): shifts within
+// rows of 16, then the row totals carried over with row broadcasts.
+__device__ __forceinline__ int wave_scan32(int x)
+{
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, true);  // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, true);  // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, true);  // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, true);  // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false); // row_bcast:15 into rows 1, 3
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false); // row_bcast:31 into rows 2, 3
+    return x;
 }
 
 template <int CDT, int D, int G, int NSTAGE, int WAVES>
@@ -219,34 +237,47 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(DecodeArgs a)
     // item: wave 0 scans the lengths 64 at a time with shuffles (no work-group
     // barrier inside); the other waves wait at the barrier below.
     if (w == 0) {
-        const long long v0 = lane < S ? (long long)items_of(a.context_lens[lane]) : 0;
-        long long cnt = wave_sum64(v0);
-        for (int base = 64; base < S; base += 64) {
-            const int s2 = base + lane;
-            cnt += wave_sum64(s2 < S ? (long long)items_of(a.context_lens[s2]) : 0);
+        // 64 lanes' item counts fit 32 bits whenever maxB * Hkv * 64 does:
+        // DPP scans then; otherwise shuffles on 64-bit values
+        const bool narrow = (long long)maxB * Hkv * 64 < (1ll << 31);
+        const int l0 = lane < S ? a.context_lens[lane] : 0;
+        long long cnt;
+        if (narrow && S <= 64) {
+            cnt = __builtin_amdgcn_readlane(wave_scan32(items_of(l0) * Hkv), 63);
+        } else {
+            cnt = wave_sum64((long long)items_of(l0) * Hkv);
+            for (int base = 64; base < S; base += 64) {
+                const int s2 = base + lane;
+                cnt += wave_sum64(s2 < S ? (long long)items_of(a.context_lens[s2]) * Hkv : 0);
+            }
         }
-        const long long tot = cnt * Hkv;
+        const long long tot = cnt;
         const long long x0 = tot * blockIdx.x / gridDim.x;
         int found = -1;
         long long fbase = 0, carry = 0;
         for (int base = 0; base < S; base += 64) {
             const int s2 = base + lane;
-            const long long v =
-                (base == 0 ? v0 : s2 < S ? (long long)items_of(a.context_lens[s2]) : 0) * Hkv;
-            long long incl = v;
+            const int l = base == 0 ? l0 : s2 < S ? a.context_lens[s2] : 0;
+            const long long v = (long long)items_of(l) * Hkv;
+            long long incl;
+            if (narrow) {
+                incl = wave_scan32((int)v);
+            } else {
+                incl = v;
 #pragma unroll
-            for (int d = 1; d < 64; d <<= 1) {
-                const long long t = __shfl_up(incl, d);
-                if (lane >= d)
-                    incl += t;
+                for (int d = 1; d < 64; d <<= 1) {
+                    const long long t = __shfl_up(incl, d);
+                    if (lane >= d)
+                        incl += t;
+                }
             }
             const long long excl = incl - v;
             const unsigned long long m =
                 __builtin_amdgcn_ballot_w64(v > 0 && carry + excl <= x0 && x0 < carry + incl);
             if (m) {
-                const int l = __builtin_ctzll(m);
-                found = base + l;
-                fbase = carry + __shfl(excl, l);
+                const int l2 = __builtin_ctzll(m);
+                found = base + l2;
+                fbase = carry + __shfl(excl, l2);
                 break;
             }
             carry += __shfl(incl, 63);
