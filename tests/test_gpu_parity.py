@@ -233,6 +233,16 @@ def test_poisoned_padding_and_widest_table():
     assert np.array_equal(decode_problem(p2), got)
 
 
+def test_wide_table_takes_the_64bit_scan():
+    # maxB * Hkv * 64 >= 2^31: the decode's start-up scan of the lengths runs
+    # on 64-bit sums instead of 32-bit ones; results must not change
+    width = (1 << 22) + 16
+    lens = [300, 17, 1000]
+    p = random_problem(11, 3, 16, 8, 64, lens, 200, "bf16", width=width)
+    got = decode_problem(p)
+    assert max_err(got, oracle_problem(p)) <= TOL["bf16"]
+
+
 def test_single_partition_vs_balanced_split():
     lens = [4000, 2000, 3000, 100]
     p = random_problem(10, 4, 32, 8, 128, lens, 1000, "bf16")
