@@ -11,9 +11,11 @@
 // Work decomposition (MI355X: 256 CUs in 8 XCDs, wave64):
 //   * The flat list of "items" is (sequence, KV head, x) where x is a
 //     16-token block (balanced mode) or a fixed partition of blocks.  A
-//     persistent grid of work-groups takes equal contiguous ranges of the
-//     list, so a 32k-token sequence is spread over many CUs as evenly as a
-//     batch of short ones.  A run of items of one (sequence, KV head) inside
+//     persistent grid of work-groups takes contiguous ranges of the list, so a
+//     32k-token sequence is spread over many CUs as evenly as a batch of short
+//     ones.  Balanced ranges are equal in "virtual" items: every (sequence, KV
+//     head) counts a few extra items ahead of its blocks, so a range that
+//     starts more segments holds fewer blocks.  A run of items of one (sequence, KV head) inside
 //     a range is a "segment".  A segment that covers its whole sequence
 //     writes the output directly; otherwise it writes a partial
 //     (max, sum, unnormalised accumulator); the work-group that delivers the
@@ -41,6 +43,13 @@ namespace pa {
 
 #ifndef DECODE_STAGES
 #define DECODE_STAGES 2  // blocks of K/V in a wave's LDS ring (the loop is written for 2)
+#endif
+#ifndef DECODE_SEGCOST
+// Virtual items charged for each (sequence, KV head), so that a range which
+// starts extra segments (each costs a hand-over) holds fewer real blocks.
+// Chosen by measurement on 64-sequence GQA batches: 2-3 shortens the slowest
+// work-group, more overshoots.
+#define DECODE_SEGCOST 2
 #endif
 #ifndef DECODE_WAVES
 #define DECODE_WAVES 4   // waves per work-group; they split a segment's blocks
@@ -184,9 +193,11 @@ struct DecodeSmem {
     float bmax[WAVES][4][8];     // row maxima (rescale path)
     float msum[WAVES][2][8];     // per-wave running max and sum
     long long total;  // item count of the call (start-up scan)
+    long long total_v;  // the same in virtual items (0: plain split)
+    long long range0, range1;  // this work-group's items [range0, range1)
     int last;
     int seg_i;
-    long long seg_base;
+    long long seg_base, seg_vbase;
 };
 
 // s_waitcnt vmcnt(N): the global->LDS loads of the ring are counted there and
@@ -233,77 +244,152 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(DecodeArgs a)
         return PB > 0 ? (nb + PB - 1) / PB : nb;
     };
 
-    // ---- total item count and the sequence holding this work-group's first
-    // item: wave 0 scans the lengths 64 at a time with shuffles (no work-group
-    // barrier inside); the other waves wait at the barrier below.
+    // ---- this work-group's range of items.  With the balanced split the
+    // ranges are equal in "virtual" items: each (sequence, KV head) counts
+    // ALPHA extra items ahead of its real ones (what a segment start costs),
+    // so a range that starts segments holds fewer real items.  Wave 0 scans
+    // the lengths 64 at a time (no work-group barrier inside), finds the
+    // sequences holding both ends of its range and the first real items at or
+    // after them; the other waves wait at the barrier below.
+    constexpr int ALPHA = DECODE_SEGCOST;
     if (w == 0) {
-        // 64 lanes' item counts fit 32 bits whenever maxB * Hkv * 64 does:
-        // DPP scans then; otherwise shuffles on 64-bit values
-        const bool narrow = (long long)maxB * Hkv * 64 < (1ll << 31);
-        const int l0 = lane < S ? a.context_lens[lane] : 0;
-        long long cnt;
-        if (narrow && S <= 64) {
-            cnt = __builtin_amdgcn_readlane(wave_scan32(items_of(l0) * Hkv), 63);
-        } else {
-            cnt = wave_sum64((long long)items_of(l0) * Hkv);
-            for (int base = 64; base < S; base += 64) {
-                const int s2 = base + lane;
-                cnt += wave_sum64(s2 < S ? (long long)items_of(a.context_lens[s2]) * Hkv : 0);
+        const long long W = gridDim.x;
+        // 64 lanes' item counts fit 32 bits whenever (maxB + ALPHA) * Hkv * 64
+        // does: DPP scans then; otherwise shuffles on 64-bit values
+        const bool narrow = (long long)(maxB + ALPHA) * Hkv * 64 < (1ll << 31);
+        auto scan = [&](long long v) -> long long {
+            if (narrow)
+                return wave_scan32((int)v);
+            long long incl = v;
+#pragma unroll
+            for (int d = 1; d < 64; d <<= 1) {
+                const long long t = __shfl_up(incl, d);
+                if (lane >= d)
+                    incl += t;
             }
-        }
-        const long long tot = cnt;
-        const long long x0 = tot * blockIdx.x / gridDim.x;
-        int found = -1;
-        long long fbase = 0, carry = 0;
+            return incl;
+        };
+        auto counts = [&](int l, long long &real, long long &virt) {
+            const int n = items_of(l);
+            real = (long long)n * Hkv;
+            virt = (long long)(n > 0 ? n + ALPHA : 0) * Hkv;
+        };
+        long long tot = 0, totv = 0;
         for (int base = 0; base < S; base += 64) {
             const int s2 = base + lane;
-            const int l = base == 0 ? l0 : s2 < S ? a.context_lens[s2] : 0;
-            const long long v = (long long)items_of(l) * Hkv;
-            long long incl;
+            long long r, v;
+            counts(s2 < S ? a.context_lens[s2] : 0, r, v);
             if (narrow) {
-                incl = wave_scan32((int)v);
+                tot += __builtin_amdgcn_readlane(wave_scan32((int)r), 63);
+                totv += __builtin_amdgcn_readlane(wave_scan32((int)v), 63);
             } else {
-                incl = v;
-#pragma unroll
-                for (int d = 1; d < 64; d <<= 1) {
-                    const long long t = __shfl_up(incl, d);
-                    if (lane >= d)
-                        incl += t;
+                tot += wave_sum64(r);
+                totv += wave_sum64(v);
+            }
+        }
+        const bool virt = PB == 0 && ALPHA > 0 && totv >= (long long)(ALPHA + 2) * W;
+        // position x of the split -> (sequence, its real / virtual starts, first
+        // real item at or after x)
+        auto locate = [&](long long x, int &seq, long long &rbase, long long &vbase) -> long long {
+            const long long T = virt ? totv : tot;
+            seq = -1;
+            rbase = tot;
+            vbase = totv;
+            if (x >= T)
+                return tot;
+            long long rc = 0, vc = 0;
+            for (int base = 0; base < S; base += 64) {
+                const int s2 = base + lane;
+                const int l = s2 < S ? a.context_lens[s2] : 0;
+                long long r, v;
+                counts(l, r, v);
+                const long long ri = scan(r), vi = scan(v);
+                const long long ex = (virt ? vi - v : ri - r), in = virt ? vi : ri;
+                const long long c0 = virt ? vc : rc;
+                const unsigned long long m =
+                    __builtin_amdgcn_ballot_w64(r > 0 && c0 + ex <= x && x < c0 + in);
+                if (m) {
+                    const int l2 = __builtin_ctzll(m);
+                    seq = base + l2;
+                    rbase = rc + __shfl(ri - r, l2);
+                    vbase = vc + __shfl(vi - v, l2);
+                    const int n = items_of(__shfl(l, l2));
+                    if (!virt)
+                        return x;
+                    const long long rel = x - vbase;
+                    const long long gq = rel / (n + ALPHA), xv = rel - gq * (n + ALPHA);
+                    return rbase + gq * n + (xv > ALPHA ? xv - ALPHA : 0);
                 }
+                rc += __shfl(ri, 63);
+                vc += __shfl(vi, 63);
             }
-            const long long excl = incl - v;
-            const unsigned long long m =
-                __builtin_amdgcn_ballot_w64(v > 0 && carry + excl <= x0 && x0 < carry + incl);
-            if (m) {
-                const int l2 = __builtin_ctzll(m);
-                found = base + l2;
-                fbase = carry + __shfl(excl, l2);
-                break;
-            }
-            carry += __shfl(incl, 63);
+            return tot;  // not reached while x < T
+        };
+        const long long T = virt ? totv : tot;
+        int seq0, seq1;
+        long long rb0, vb0, rb1, vb1;
+        long long r0, r1;
+        if (narrow && S <= 64) {
+            // one pass: both prefix sums once, totals and the found lane read
+            // with scalar lane reads
+            const int l = lane < S ? a.context_lens[lane] : 0;
+            long long rr, vv;
+            counts(l, rr, vv);
+            const int ri = wave_scan32((int)rr), vi = wave_scan32((int)vv);
+            const int n = items_of(l);
+            auto find = [&](long long x, int &seq, long long &rbase, long long &vbase) -> long long {
+                seq = -1;
+                rbase = tot;
+                vbase = totv;
+                if (x >= T)
+                    return tot;
+                const long long in = virt ? vi : ri, ex = in - (virt ? vv : rr);
+                const unsigned long long m = __builtin_amdgcn_ballot_w64(rr > 0 && ex <= x && x < in);
+                const int l2 = __builtin_ctzll(m);  // m != 0 while x < T
+                seq = l2;
+                rbase = __builtin_amdgcn_readlane(ri, l2) - __builtin_amdgcn_readlane((int)rr, l2);
+                vbase = __builtin_amdgcn_readlane(vi, l2) - __builtin_amdgcn_readlane((int)vv, l2);
+                if (!virt)
+                    return x;
+                const int nn = __builtin_amdgcn_readlane(n, l2);
+                const long long rel = x - vbase;
+                const long long gq = rel / (nn + ALPHA), xv = rel - gq * (nn + ALPHA);
+                return rbase + gq * nn + (xv > ALPHA ? xv - ALPHA : 0);
+            };
+            r0 = find(T * blockIdx.x / W, seq0, rb0, vb0);
+            r1 = find(T * (blockIdx.x + 1) / W, seq1, rb1, vb1);
+        } else {
+            r0 = locate(T * blockIdx.x / W, seq0, rb0, vb0);
+            r1 = locate(T * (blockIdx.x + 1) / W, seq1, rb1, vb1);
         }
         if (lane == 0) {
             sm.total = tot;
-            sm.seg_i = found;
-            sm.seg_base = fbase;
+            sm.total_v = virt ? totv : 0;
+            sm.range0 = r0;
+            sm.range1 = r1;
+            sm.seg_i = seq0;
+            sm.seg_base = rb0;
+            sm.seg_vbase = vb0;
         }
     }
     barrier_lds();
     const long long total = uniform64(sm.total);
+    const long long total_v = uniform64(sm.total_v);  // > 0: virtual split
     if (blockIdx.x == 0) {  // sequences with no tokens get a zero output row
         for (int i = tid; i < S; i += NT)
             if (a.context_lens[i] <= 0)
                 for (int e = 0; e < Hq * D; ++e)
                     a.out[(int64_t)i * Hq * D + e] = 0.f;
     }
-    const long long a0 = total * blockIdx.x / gridDim.x;
-    const long long a1 = total * (blockIdx.x + 1) / gridDim.x;
+    const long long a0 = uniform64(sm.range0);
+    const long long a1 = uniform64(sm.range1);
     if (a0 >= a1)
         return;
     int i = uniform(sm.seg_i);
     if (i < 0)  // unreachable while a0 < total; keeps every index in range
         return;
-    long long base_i = uniform64(sm.seg_base);  // first item index of sequence i
+    long long base_i = uniform64(sm.seg_base);    // first item index of sequence i
+    long long vbase_i = uniform64(sm.seg_vbase);  // its first virtual item
     long long item = a0;
     const int lane_m = head_mask<LPT, GP>(lane);
     const bool lane_owner = mask_owner<LPT, GP>(lane) && lane_m < G;
@@ -375,7 +461,8 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(DecodeArgs a)
             // least as many items as work-groups every range is non-empty (rank =
             // blockIdx.x); with fewer, each non-empty range holds one item (rank =
             // a0).  Ranks keep the partial slots of one (sequence, head) contiguous.
-            d.slot = (int)(a0 < (long long)blockIdx.x ? a0 : (long long)blockIdx.x) + si * Hkv + d.g;
+            d.slot = (int)(total_v > 0 || a0 >= (long long)blockIdx.x ? (long long)blockIdx.x : a0) +
+                     si * Hkv + d.g;
         }
         d.b0 = uniform(d.b0);
         d.b1 = uniform(d.b1);
@@ -460,9 +547,10 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(DecodeArgs a)
         const long long item_n = item + seg_items;
         const bool has_next = item_n < a1;
         int i_n = i;
-        long long base_n = base_i;
+        long long base_n = base_i, vbase_n = vbase_i;
         if (last && g == Hkv - 1) {
             base_n += (long long)n_i * Hkv;
+            vbase_n += (long long)(n_i + ALPHA) * Hkv;
             ++i_n;
         }
         Seg nx = sg;
@@ -819,14 +907,23 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(DecodeArgs a)
                 hi = lo + n_i - 1;
             } else {
                 const long long W = gridDim.x;
-                const long long first_item = base_i + (long long)g * n_i;
-                const long long last_item = first_item + n_i - 1;
-                const long long k_first = ((first_item + 1) * W - 1) / total;
-                const long long k_last = ((last_item + 1) * W - 1) / total;
-                const long long r_first = k_first < k_first * total / W ? k_first : k_first * total / W;
-                const long long r_last = k_last < k_last * total / W ? k_last : k_last * total / W;
-                lo = (int)r_first + pair;
-                hi = (int)r_last + pair;
+                if (total_v > 0) {
+                    // work-groups whose (virtual) ranges hold the pair's real items;
+                    // every range holds at least one real item, so rank = index
+                    const long long first_v = vbase_i + (long long)g * (n_i + ALPHA) + ALPHA;
+                    const long long last_v = first_v + n_i - 1;
+                    lo = (int)(((first_v + 1) * W - 1) / total_v) + pair;
+                    hi = (int)(((last_v + 1) * W - 1) / total_v) + pair;
+                } else {
+                    const long long first_item = base_i + (long long)g * n_i;
+                    const long long last_item = first_item + n_i - 1;
+                    const long long k_first = ((first_item + 1) * W - 1) / total;
+                    const long long k_last = ((last_item + 1) * W - 1) / total;
+                    const long long r_first = k_first < k_first * total / W ? k_first : k_first * total / W;
+                    const long long r_last = k_last < k_last * total / W ? k_last : k_last * total / W;
+                    lo = (int)r_first + pair;
+                    hi = (int)r_last + pair;
+                }
             }
             wait_vm<0>();
             barrier_lds();
@@ -895,6 +992,7 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(DecodeArgs a)
         item = item_n;
         i = i_n;
         base_i = base_n;
+        vbase_i = vbase_n;
         sg = nx;
         qbi ^= 1;
     }
