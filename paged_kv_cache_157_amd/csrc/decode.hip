@@ -998,13 +998,21 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(DecodeArgs a)
     }
 }
 
-int64_t decode_partial_slots(int num_seqs, int num_kv_heads, int max_blocks, int part_blocks,
-                             int grid)
+int decode_hpg(int num_kv_heads, int group)
+{
+    return num_kv_heads % 4 == 0 && num_kv_heads >= 8 && group >= 2 ? 4 : 1;
+}
+
+int64_t decode_partial_slots(int num_seqs, int num_kv_heads, int group, int max_blocks,
+                             int part_blocks, int grid)
 {
     const int64_t pairs = (int64_t)num_seqs * num_kv_heads;
-    if (part_blocks > 0)
+    if (part_blocks > 0)  // one record per (partition, sequence, KV head)
         return pairs * ((max_blocks + part_blocks - 1) / part_blocks);
-    return (int64_t)grid + pairs;
+    // balanced split: a record per (range, sequence, KV head) that a range
+    // can start a segment of, times the heads of one work-group
+    const int hpg = decode_hpg(num_kv_heads, group);
+    return ((int64_t)grid + pairs / hpg) * hpg;
 }
 
 bool decode_supported(int cache_dtype, int head_dim, int group)
@@ -1042,8 +1050,10 @@ static DecodeKernels kernels_d(int G)
     }
 }
 
-DecodeKernels decode_kernels(int cache_dtype, int head_dim, int group)
+DecodeKernels decode_kernels(int cache_dtype, int head_dim, int group, int hpg)
 {
+    if (hpg == 4)
+        return decode_hg4_kernels(cache_dtype, head_dim, group);
     if (cache_dtype == DT_F32)
         return kernels_d<DT_F32, 64>(group);
     if (cache_dtype == DT_BF16)
@@ -1061,7 +1071,8 @@ DecodeKernels decode_kernels(int cache_dtype, int head_dim, int group)
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream)
 {
-    const DecodeKernels k = decode_kernels(a.cache_dtype, a.head_dim, a.num_q_heads / a.num_kv_heads);
+    const int G = a.num_q_heads / a.num_kv_heads;
+    const DecodeKernels k = decode_kernels(a.cache_dtype, a.head_dim, G, decode_hpg(a.num_kv_heads, G));
     DecodeArgs args = a;
     void *params[] = {&args};
     return hipLaunchKernel(k.main, dim3(a.grid), dim3(k.threads), params, 0, stream);

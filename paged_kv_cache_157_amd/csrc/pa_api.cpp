@@ -61,17 +61,18 @@ int device_cus()
 int decode_grid(const pa_shape *s)
 {
     static std::mutex mu;
-    static int cached[64][3][2][9] = {};
+    static int cached[64][3][2][9][2] = {};
     const int G = s->num_q_heads / s->num_kv_heads;
+    const int hpg = pa::decode_hpg(s->num_kv_heads, G);
     const int dt = s->cache_dtype, dh = s->head_dim == 128 ? 1 : 0;
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
         return 256;
     std::lock_guard<std::mutex> lock(mu);
-    int &slot = cached[dev][dt][dh][G];
+    int &slot = cached[dev][dt][dh][G][hpg == 4];
     if (slot == 0) {
         int per_cu = 0;
-        const pa::DecodeKernels k = pa::decode_kernels(dt, s->head_dim, G);
+        const pa::DecodeKernels k = pa::decode_kernels(dt, s->head_dim, G, hpg);
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k.main, k.threads, 0) !=
                 hipSuccess ||
             per_cu <= 0)
@@ -123,7 +124,7 @@ DecodeLayout decode_layout(const pa_shape *s)
     const int G = s->num_q_heads / s->num_kv_heads;
     const int pb = s->partition_tokens > 0 ? s->partition_tokens / 16 : 0;
     DecodeLayout L;
-    L.slots = pa::decode_partial_slots(s->num_seqs, s->num_kv_heads, s->max_blocks_per_seq, pb,
+    L.slots = pa::decode_partial_slots(s->num_seqs, s->num_kv_heads, G, s->max_blocks_per_seq, pb,
                                        decode_grid(s));
     L.count_bytes = (size_t)pa::kDecodeCounterSlots * sizeof(int32_t);
     L.ml_bytes = align256((size_t)L.slots * G * 2 * sizeof(float));

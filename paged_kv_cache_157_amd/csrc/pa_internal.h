@@ -32,22 +32,27 @@ struct DecodeArgs {
     int grid;              // persistent work-group count
     float qk_scale;        // softmax scale * log2(e) (* kv_scale for fp8 K)
     float v_scale;         // 1, or kv_scale for fp8 V
-    float *ws_acc;         // [slots][G][D]
-    float *ws_ml;          // [slots][G][2]
-    int32_t *ws_count;     // [S * Hkv] arrival counters, zero between calls
+    float *ws_acc;         // [records][G][D]
+    float *ws_ml;          // [records][G][2]
+    int32_t *ws_count;     // arrival counters (at most S * Hkv), zero between calls
 };
 // Arrival counters sit at the start of every decode workspace; this region
 // must be zero before the first call and every call leaves it zero.
 constexpr int64_t kDecodeCounterSlots = 1 << 20;
-// Number of partial-result slots the decode workspace must hold.
-int64_t decode_partial_slots(int num_seqs, int num_kv_heads, int max_blocks, int part_blocks,
-                             int grid);
+// Number of partial-result records the decode workspace must hold.
+int64_t decode_partial_slots(int num_seqs, int num_kv_heads, int group, int max_blocks,
+                             int part_blocks, int grid);
 bool decode_supported(int cache_dtype, int head_dim, int group);
 struct DecodeKernels {
     const void *main;    // persistent split-K decode kernel (merges its own partials)
     int threads;         // work-group size
 };
-DecodeKernels decode_kernels(int cache_dtype, int head_dim, int group);
+// KV heads one decode work-group serves: 4 (the head-group kernel) when the
+// model has at least two groups of four KV heads and G >= 2, else 1.
+int decode_hpg(int num_kv_heads, int group);
+DecodeKernels decode_kernels(int cache_dtype, int head_dim, int group, int hpg);
+// the head-group kernels (decode_hg4.hip)
+DecodeKernels decode_hg4_kernels(int cache_dtype, int head_dim, int group);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
 
 struct PrefillArgs {

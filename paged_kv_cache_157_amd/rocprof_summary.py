@@ -27,7 +27,7 @@ TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
 
 def decode_source_hash() -> str:
     h = hashlib.sha256()
-    for f in ("decode.hip", "pa_device.h"):
+    for f in ("decode.hip", "decode_hg.h", "decode_hg4.hip", "pa_device.h"):
         h.update(open(os.path.join(HERE, "csrc", f), "rb").read())
     return h.hexdigest()[:16]
 

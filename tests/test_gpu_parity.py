@@ -173,14 +173,18 @@ COMBOS = ([("f32", 64, G) for G in (1, 2, 3, 4, 5, 6, 7, 8)] +
           [("bf16", d, G) for d in (64, 128) for G in (1, 2, 3, 4, 5, 6, 7, 8)] +
           [("fp8", 128, G) for G in (1, 2, 3, 4, 5, 6, 7, 8)] +
           [("fp8", 64, G) for G in (1, 2, 3, 4)])
+# two KV heads run the one-head-per-work-group kernel; eight KV heads with
+# G >= 2 run the kernel that takes four KV heads per work-group
+SWEEP = ([(s, d, G, 2) for s, d, G in COMBOS] +
+         [(s, d, G, 8) for s, d, G in COMBOS if G >= 2])
 
 
-@pytest.mark.parametrize("storage,d,G", COMBOS)
-def test_group_and_dtype_sweep(storage, d, G):
-    hkv = 2
+@pytest.mark.parametrize("storage,d,G,hkv", SWEEP)
+def test_group_and_dtype_sweep(storage, d, G, hkv):
     lens = [1, 15, 16, 17, 100, 333, 0, 64 * 16]
-    p = random_problem(1000 + G * 10 + d, len(lens), G * hkv, hkv, d, lens, 256, storage)
-    say(f"sweep {storage} d={d} G={G}")
+    nb = 256 if hkv == 2 else 128
+    p = random_problem(1000 + G * 10 + d + hkv, len(lens), G * hkv, hkv, d, lens, nb, storage)
+    say(f"sweep {storage} d={d} G={G} Hkv={hkv}")
     got = decode_problem(p)
     ref = oracle_problem(p)
     assert np.all(got[6] == 0.0)  # L = 0 gives a zero row
@@ -235,10 +239,11 @@ def test_poisoned_padding_and_widest_table():
 
 def test_wide_table_takes_the_64bit_scan():
     # maxB * Hkv * 64 >= 2^31: the decode's start-up scan of the lengths runs
-    # on 64-bit sums instead of 32-bit ones; results must not change
+    # on 64-bit sums instead of 32-bit ones; results must not change (G = 1,
+    # so the one-head-per-work-group kernel serves it)
     width = (1 << 22) + 16
     lens = [300, 17, 1000]
-    p = random_problem(11, 3, 16, 8, 64, lens, 200, "bf16", width=width)
+    p = random_problem(11, 3, 8, 8, 64, lens, 200, "bf16", width=width)
     got = decode_problem(p)
     assert max_err(got, oracle_problem(p)) <= TOL["bf16"]
 
@@ -324,10 +329,11 @@ def test_prefill_peaked_scores(storage):
     assert max_err(out.cpu().numpy(), ref) <= TOL[storage]
 
 
+@pytest.mark.parametrize("hkv", [4, 8])
 @pytest.mark.parametrize("storage", ["bf16", "fp8"])
-def test_decode_peaked_scores(storage):
-    p = random_problem(22, 6, 28, 4, 128, [1, 17, 300, 1000, 2049, 4000], 1200, storage)
+def test_decode_peaked_scores(storage, hkv):
+    p = random_problem(22, 6, 7 * hkv, hkv, 128, [1, 17, 300, 1000, 2049, 4000], 1200, storage)
     p["scale"] = 1.0
-    say(f"decode peaked {storage}")
+    say(f"decode peaked {storage} Hkv={hkv}")
     out = decode_problem(p)
     assert max_err(out, oracle_problem(p)) <= TOL[storage]
