@@ -13,7 +13,8 @@ Prints one JSON line.  `value` is the effective KV bandwidth of the step: KV
 bytes the decode must read (each sequence's K and V rows, once) divided by
 the step time.  The roofline entry is for the decode launch (its two
 kernels), timed with HIP events on the stream the kernels run on, in a
-second pass right after the timed steps.
+second pass right after the timed steps.  The cache write, shorter than one
+host submission, is timed over 200 launches queued behind a GPU-side wait.
 """
 from __future__ import annotations
 
@@ -163,12 +164,29 @@ def main():
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
 
-    def launch_ms(fn, n):
+    # GPU-side wait: torch.cuda._sleep spins for a number of GPU clock ticks;
+    # ticks per millisecond are measured once here
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    probe_ticks = 1 << 22
+    torch.cuda._sleep(probe_ticks)
+    e0.record()
+    torch.cuda._sleep(probe_ticks)
+    e1.record()
+    torch.cuda.synchronize()
+    ticks_per_ms = probe_ticks / max(e0.elapsed_time(e1), 1e-3)
+
+    def launch_ms(fn, n, hold=False):
         """Average duration of one launch of fn: HIP events recorded on the stream
         the kernels run on (torch's current stream) around n back-to-back launches
-        (one event pair, so the event cost is spread over n launches)."""
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        (one event pair, so the event cost is spread over n launches).  With
+        `hold`, the launches are queued behind a GPU-side wait long enough for
+        the host to submit all of them, so that a kernel shorter than one host
+        submission (the cache write) is timed on the GPU and not at the host's
+        pace.  Longer kernels are timed without it: the GPU is then the
+        bottleneck anyway, and an idle wait lets its clocks drop."""
         fn()
+        if hold:
+            torch.cuda._sleep(int(ticks_per_ms * (0.5 + 0.03 * n)))
         e0.record()
         for _ in range(n):
             fn()
@@ -178,7 +196,8 @@ def main():
 
     dec_ms = launch_ms(decode, args.steps)
     pre_ms = launch_ms(prefill, args.steps) if out_pre is not None else None
-    cw_ms = launch_ms(cache_write, args.steps)
+    # held launches: at most 200 per event pair (HIP's queue depth)
+    cw_ms = launch_ms(cache_write, min(args.steps, 200), hold=True)
     if args.copy_probe_mib:
         # a plain device copy of known size: rocprofv3 --pmc reads of FETCH_SIZE /
         # WRITE_SIZE for it convert the counters into bytes
