@@ -259,6 +259,46 @@ def test_single_partition_vs_balanced_split():
 
 
 # ----------------------------------------------------------------------------
+# fixed partitions in the head-group kernel (8 KV heads, G = 4: 512 work-groups
+# on MI355X): results are reproducible bit for bit and every call leaves the
+# arrival counters zero, with more partitions than two per work-group, between
+# one and two, and fewer than one.
+# ----------------------------------------------------------------------------
+
+def _decode_counters_zero() -> bool:
+    torch.cuda.synchronize()
+    ws = binding._workspaces[(torch.cuda.current_device(), "decode")]
+    return bool((ws[: 4 << 20] == 0).all().item())
+
+
+@pytest.mark.parametrize("lens,ptok", [
+    ([16 * 300, 40, 16 * 2048, 5, 16 * 77], 16),   # 4,858 partitions
+    ([16 * 500, 16 * 300], 32),                     # 800
+    ([16 * 500, 16 * 300], 512),                    # 52
+])
+def test_fixed_partitions_are_reproducible(lens, ptok):
+    p = random_problem(31, len(lens), 32, 8, 128, lens, 2500, "bf16")
+    say(f"fixed partitions of {ptok} tokens")
+    a = decode_problem(p, partition_tokens=ptok)
+    assert _decode_counters_zero()
+    b = decode_problem(p, partition_tokens=ptok)
+    assert _decode_counters_zero()
+    assert np.array_equal(a, b)
+    assert max_err(a, oracle_problem(p)) <= TOL["bf16"]
+
+
+def test_partitions_of_many_short_sequences():
+    rng = np.random.default_rng(32)
+    lens = [int(x) for x in rng.integers(1, 100, 1100)]
+    lens[5] = 0
+    p = random_problem(32, len(lens), 16, 8, 64, lens, 8000, "bf16")
+    got = decode_problem(p, partition_tokens=32)
+    assert _decode_counters_zero()
+    assert np.all(got[5] == 0.0)
+    assert max_err(got, oracle_problem(p)) <= TOL["bf16"]
+
+
+# ----------------------------------------------------------------------------
 # chunked prefill special cases
 # ----------------------------------------------------------------------------
 
