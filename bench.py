@@ -31,6 +31,7 @@ from paged_kv_cache_157_amd import binding
 from paged_kv_cache_157_amd.workload import CONFIGS, apply_cow, kv_bytes_per_token, make_step
 
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
 METRIC = "paged decode attention: effective KV HBM GB/s (% of peak) and tokens/s, 1 GPU"
 HOST_CORE_SHARE = 16
 
@@ -61,6 +62,37 @@ def algorithmic_bytes(cfg, step) -> dict:
     out = cfg.num_seqs * cfg.num_q_heads * cfg.head_dim * 4
     tables = int(((L + 15) // 16).sum()) * 4 + 4 * cfg.num_seqs
     return dict(kv=kv, total=kv + q + out + tables)
+
+
+def unique_kv_bytes(cfg, step) -> int:
+    """KV bytes of the distinct physical blocks the decode reads: a block
+    shared by several sequences (a common prefix) counts once, with the
+    largest number of its slots any of them uses."""
+    L = step.plan.context_lens.astype(np.int64)
+    bt = step.plan.block_tables
+    phys, fill = [], []
+    for i, l in enumerate(L):
+        nb = int((l + 15) // 16)
+        j = np.arange(nb)
+        phys.append(bt[i, :nb].astype(np.int64))
+        fill.append(np.minimum(16, l - 16 * j))
+    phys = np.concatenate(phys)
+    fill = np.concatenate(fill)
+    best = np.zeros(cfg.num_blocks, np.int64)
+    np.maximum.at(best, phys, fill)
+    return int(best.sum()) * kv_bytes_per_token(cfg)
+
+
+def partial_bytes(cfg, step) -> int:
+    """With fixed partitions: bytes of the split-K partial records, each
+    (max, sum, accumulator) of G query heads written once and read once, for
+    every partition of a (sequence, KV head) that has more than one."""
+    pt = cfg.partition_tokens
+    if pt <= 0:
+        return 0
+    parts = (step.plan.context_lens.astype(np.int64) + pt - 1) // pt
+    G = cfg.num_q_heads // cfg.num_kv_heads
+    return int(parts[parts > 1].sum()) * cfg.num_kv_heads * G * (cfg.head_dim + 2) * 4 * 2
 
 
 def cpu_baseline(cfg, step) -> dict:
@@ -198,6 +230,44 @@ def main():
     pre_ms = launch_ms(prefill, args.steps) if out_pre is not None else None
     # held launches: at most 200 per event pair (HIP's queue depth)
     cw_ms = launch_ms(cache_write, min(args.steps, 200), hold=True)
+
+    def cold_us(fn, evict, n=20, reps=5):
+        """Launch time of fn with its inputs evicted from the 256 MB Infinity
+        Cache: n rounds of (a read of `evict`, larger than that cache, then fn)
+        back to back, minus n reads alone, per round; median and minimum over
+        `reps` repetitions."""
+        ts = []
+        for _ in range(reps):
+            t = []
+            for with_fn in (True, False):
+                evict.sum()
+                torch.cuda.synchronize()
+                e0.record()
+                for _ in range(n):
+                    evict.sum()
+                    if with_fn:
+                        fn()
+                e1.record()
+                torch.cuda.synchronize()
+                t.append(e0.elapsed_time(e1))
+            ts.append((t[0] - t[1]) / n * 1e3)
+        return dict(median=round(float(np.median(ts)), 2), min=round(float(np.min(ts)), 2),
+                    rounds=n * reps)
+
+    evict = torch.ones(192 << 20, dtype=torch.float32, device=dev)  # 768 MiB
+    dec_cold = cold_us(decode, evict)
+    del evict
+    # read-stream context: a plain 1 GiB device copy (reads and writes 1 GiB)
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    e0.record()
+    for _ in range(5):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_gbs = 2 * (1 << 30) * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
     if args.copy_probe_mib:
         # a plain device copy of known size: rocprofv3 --pmc reads of FETCH_SIZE /
         # WRITE_SIZE for it convert the counters into bytes
@@ -207,7 +277,9 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
 
+    tokens_per_step = cfg.num_seqs + (cfg.prefill_chunk if out_pre is not None else 0)
     ab = algorithmic_bytes(cfg, step)
+    uniq = unique_kv_bytes(cfg, step)
     kv_gbs = ab["kv"] / (ms_per_step * 1e-3) / 1e9
     achieved = ab["total"] / (dec_ms * 1e-3) / 1e9
     traffic = None
@@ -239,8 +311,13 @@ def main():
                    "context_tokens": int(step.plan.context_lens.sum()),
                    "new_tokens": int(len(step.plan.slot_mapping)), "seed": cfg.seed},
         "pct_of_hbm_peak": round(100.0 * kv_gbs / HBM_PEAK_GBS, 2),
-        "tokens_per_s": round(cfg.num_seqs / (ms_per_step * 1e-3), 1),
+        "tokens_per_step": tokens_per_step,
+        "tokens_per_s": round(tokens_per_step / (ms_per_step * 1e-3), 1),
         "decode_us": round(dec_ms * 1e3, 2),
+        # with the Infinity Cache evicted before every launch (decode_us: warm)
+        "decode_cold_us": dec_cold,
+        "decode_cold_kv_gbs": round(ab["kv"] / (dec_cold["median"] * 1e-6) / 1e9, 2),
+        "device_copy_gbs": round(copy_gbs, 1),
         "cache_write_us": round(cw_ms * 1e3, 2),
         "decode_kv_gbs": round(ab["kv"] / (dec_ms * 1e-3) / 1e9, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
@@ -248,11 +325,17 @@ def main():
                      "traffic": traffic, "kernel": "pa_decode (decode_kernel, one launch)",
                      "algorithmic_bytes_per_launch": ab["total"]},
     }
+    if uniq < ab["kv"]:  # shared blocks: the distinct bytes read as well
+        res["unique_kv_bytes"] = uniq
+        res["decode_unique_kv_gbs"] = round(uniq / (dec_ms * 1e-3) / 1e9, 2)
+    if cfg.partition_tokens > 0:
+        res["partial_bytes_per_launch"] = partial_bytes(cfg, step)
     if pre_ms is not None:
         g = cfg.num_q_heads * cfg.head_dim * 4 * sum(
             cfg.prefill_history + j + 1 for j in range(cfg.prefill_chunk))
         res["prefill_us"] = round(pre_ms * 1e3, 2)
         res["prefill_tflops"] = round(g / (pre_ms * 1e-3) / 1e12, 2)
+        res["prefill_pct_of_bf16_mfma_peak"] = round(100.0 * res["prefill_tflops"] / MFMA_BF16_PEAK_TFLOPS, 2)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(cfg, step)
     print(json.dumps(res), flush=True)
