@@ -254,6 +254,22 @@ def main():
         return dict(median=round(float(np.median(ts)), 2), min=round(float(np.min(ts)), 2),
                     rounds=n * reps)
 
+    # copy-on-write copies (pa_copy_blocks): up to 1024 pairs from blocks the
+    # batch uses into free blocks, so no table's data changes
+    free = step.plan.pool.free_blocks()[:1024]
+    used = np.unique(step.plan.block_tables[step.plan.block_tables >= 0])
+    copy_res = None
+    if free and len(used):
+        rng = np.random.default_rng(cfg.seed)
+        pairs = np.stack([rng.choice(used, len(free)), np.array(free)], 1).astype(np.int64)
+        pairs_d = torch.from_numpy(pairs).to(dev)
+        blk = kv_bytes_per_token(cfg) // 2 * 16  # one block of one pool
+        cp_ms = launch_ms(lambda: binding.copy_blocks(step.k_cache, step.v_cache, pairs_d),
+                          min(args.steps, 200), hold=True)
+        moved = 2 * 2 * len(free) * blk  # both pools, read and write
+        copy_res = dict(pairs=len(free), us=round(cp_ms * 1e3, 2),
+                        gbs=round(moved / (cp_ms * 1e-3) / 1e9, 1))
+
     evict = torch.ones(192 << 20, dtype=torch.float32, device=dev)  # 768 MiB
     dec_cold = cold_us(decode, evict)
     del evict
@@ -319,6 +335,7 @@ def main():
         "decode_cold_kv_gbs": round(ab["kv"] / (dec_cold["median"] * 1e-6) / 1e9, 2),
         "device_copy_gbs": round(copy_gbs, 1),
         "cache_write_us": round(cw_ms * 1e3, 2),
+        "copy_blocks": copy_res,
         "decode_kv_gbs": round(ab["kv"] / (dec_ms * 1e-3) / 1e9, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),

@@ -96,6 +96,23 @@ pa_status pa_reshape_and_cache(const void *k, const void *v, void *k_cache, void
                                const int64_t *slot_mapping, int64_t num_tokens,
                                int32_t src_dtype, const pa_shape *shape, void *stream);
 
+/*
+ * pa_copy_blocks -- copy whole KV blocks inside both pools (copy-on-write).
+ *   [L33] §2.4: before a sequence writes into a block that other sequences
+ *   still reference (ref_cnt > 1), the block is copied to a private one and
+ *   the writer's table points there; [VM] §3.4 the same for a forked prefix.
+ *   k_cache, v_cache: the pools, [num_blocks, 16, num_kv_heads, head_dim]
+ *   block_pairs:   [num_pairs, 2] int64 device array of (src, dst) block ids;
+ *                  k_cache[dst] = k_cache[src] and v_cache[dst] = v_cache[src]
+ *   The copies run concurrently: dst ids must be distinct and no dst may be
+ *   the src of another pair (else the result is unspecified).  A pair with
+ *   an id outside [0, num_blocks) is skipped.  The shape is validated as for
+ *   pa_reshape_and_cache; the copy uses its num_blocks, num_kv_heads,
+ *   head_dim and cache_dtype.  num_pairs == 0 is a no-op.
+ */
+pa_status pa_copy_blocks(void *k_cache, void *v_cache, const int64_t *block_pairs,
+                         int64_t num_pairs, const pa_shape *shape, void *stream);
+
 /* Workspace bytes pa_decode needs for this shape (depends on the shape and
  * on the device's compute-unit count only). */
 size_t pa_decode_workspace_bytes(const pa_shape *shape);

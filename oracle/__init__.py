@@ -50,6 +50,8 @@ def _load():
         lib.oracle_reshape_and_cache.argtypes = [P, P, P, P, P, i64, ctypes.c_int, ctypes.c_int,
                                                  ctypes.c_int, ctypes.c_int, flt]
         lib.oracle_reshape_and_cache.restype = None
+        lib.oracle_copy_blocks.argtypes = [P, P, P, i64, i64, i64]
+        lib.oracle_copy_blocks.restype = None
         lib.oracle_decode.argtypes = [P, P, ctypes.c_int, P, P, ctypes.c_int, dbl, P, i32, P,
                                       ctypes.c_int, ctypes.c_int, ctypes.c_int, dbl, P, P, i64,
                                       ctypes.c_int]
@@ -103,6 +105,18 @@ def reshape_and_cache(k, v, k_cache, v_cache, slot_mapping, kv_scale: float = 1.
     _load().oracle_reshape_and_cache(_ptr(k), _ptr(v), _ptr(k_cache), _ptr(v_cache),
                                      _ptr(slot_mapping), T, _dtype_code(k),
                                      _dtype_code(k_cache), hkv, d, float(kv_scale))
+
+
+def copy_blocks(k_cache, v_cache, pairs) -> None:
+    """Copy-on-write of whole blocks in host pools ([slots, Hkv, d], 16 slots
+    per block), in place: for each (src, dst) row of ``pairs``, in order,
+    block dst of both pools becomes a copy of block src."""
+    pairs = np.ascontiguousarray(np.asarray(pairs, dtype=np.int64).reshape(-1, 2))
+    assert v_cache.shape == k_cache.shape and v_cache.dtype == k_cache.dtype
+    assert k_cache.shape[0] % 16 == 0
+    block_bytes = 16 * k_cache.shape[1] * k_cache.shape[2] * k_cache.itemsize
+    _load().oracle_copy_blocks(_ptr(k_cache), _ptr(v_cache), _ptr(pairs), pairs.shape[0],
+                               k_cache.shape[0] // 16, block_bytes)
 
 
 def decode(q, k_cache, v_cache, block_tables, context_lens, scale, kv_scale=1.0,

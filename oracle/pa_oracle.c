@@ -171,6 +171,24 @@ void oracle_reshape_and_cache(const void *k, const void *v, void *k_cache, void 
     }
 }
 
+/* Copy-on-write ([L33] §2.4): for every (src, dst) pair, in order, the 16
+ * token rows of block src in both pools are copied over the rows of block
+ * dst (pools [num_slots, Hkv, d], block b = slots 16b .. 16b + 15).  A pair
+ * naming a block outside [0, num_blocks) is skipped. */
+void oracle_copy_blocks(void *k_cache, void *v_cache, const int64_t *pairs, int64_t num_pairs,
+                        int64_t num_blocks, int64_t block_bytes)
+{
+    for (int64_t p = 0; p < num_pairs; ++p) {
+        int64_t src = pairs[2 * p], dst = pairs[2 * p + 1];
+        if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks)
+            continue;
+        memmove((char *)k_cache + dst * block_bytes, (const char *)k_cache + src * block_bytes,
+                (size_t)block_bytes);
+        memmove((char *)v_cache + dst * block_bytes, (const char *)v_cache + src * block_bytes,
+                (size_t)block_bytes);
+    }
+}
+
 /* ------------------------------------------------------------------ */
 /* Attention over a paged history                                     */
 /* ------------------------------------------------------------------ */

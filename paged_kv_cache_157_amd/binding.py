@@ -67,6 +67,8 @@ def load() -> ctypes.CDLL:
         lib.pa_prefill_workspace_bytes.restype = sz
         lib.pa_prefill_chunk.argtypes = [P, P, P, P, P, P, P, i64, f32, S, P, sz, P]
         lib.pa_prefill_chunk.restype = ctypes.c_int
+        lib.pa_copy_blocks.argtypes = [P, P, P, i64, S, P]
+        lib.pa_copy_blocks.restype = ctypes.c_int
         lib.pa_status_string.argtypes = [ctypes.c_int]
         lib.pa_status_string.restype = ctypes.c_char_p
         lib.pa_last_error.argtypes = []
@@ -151,6 +153,23 @@ def reshape_and_cache(k: torch.Tensor, v: torch.Tensor, k_cache: torch.Tensor,
     _check(lib.pa_reshape_and_cache(_ptr(k), _ptr(v), _ptr(k_cache), _ptr(v_cache),
                                     _ptr(slot_mapping), k.shape[0], _DTYPES[k.dtype],
                                     ctypes.byref(shape), _stream(dev)))
+
+
+def copy_blocks(k_cache: torch.Tensor, v_cache: torch.Tensor, block_pairs: torch.Tensor) -> None:
+    """pa_copy_blocks: k_cache[dst] = k_cache[src], v_cache[dst] = v_cache[src] for
+    every (src, dst) row of block_pairs ([n, 2] int64 on the pools' device)."""
+    dev = k_cache.device
+    _require(k_cache, "k_cache", dev)
+    _require(v_cache, "v_cache", dev)
+    _require(block_pairs, "block_pairs", dev, torch.int64, 2)
+    if block_pairs.shape[1] != 2:
+        raise ValueError("block_pairs must be [n, 2] (src, dst)")
+    if v_cache.shape != k_cache.shape or v_cache.dtype != k_cache.dtype:
+        raise ValueError("k_cache and v_cache must match")
+    q_dtype = torch.float32 if k_cache.dtype == torch.float32 else torch.bfloat16
+    shape = make_shape(k_cache.shape[2], k_cache, q_dtype, 0, 1)
+    _check(load().pa_copy_blocks(_ptr(k_cache), _ptr(v_cache), _ptr(block_pairs),
+                                 block_pairs.shape[0], ctypes.byref(shape), _stream(dev)))
 
 
 def decode_workspace_bytes(shape: PAShape) -> int:

@@ -73,6 +73,10 @@ class BlockPool:
     def ref_counts(self) -> np.ndarray:
         return self._ref.copy()
 
+    def free_blocks(self) -> List[int]:
+        """The free queue, head first (the order allocations take them)."""
+        return list(self._free)
+
     # -- verbs -------------------------------------------------------------
     def allocate(self, n: int) -> List[int]:
         """Pop ``n`` blocks from the head of the free queue, ref_cnt = 1."""

@@ -19,7 +19,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libpa.so")
-SOURCES = ["decode_hg4.hip", "decode.hip", "prefill.hip", "reshape.hip", "pa_api.cpp"]
+SOURCES = ["decode_hg4.hip", "decode.hip", "prefill.hip", "reshape.hip", "copy_blocks.hip",
+           "pa_api.cpp"]
 ARCH = "gfx950"
 
 
@@ -56,7 +57,7 @@ def build(verbose: bool = True, defines=(), out: str = LIB) -> str:
     `defines` are extra -D switches (tuning constants such as DECODE_STAGES)."""
     obj_dir = os.path.join(HERE, "_build" if not defines else "_build_" + "_".join(defines))
     os.makedirs(obj_dir, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(5, len(SOURCES))) as ex:
+    with cf.ThreadPoolExecutor(max_workers=min(6, len(SOURCES))) as ex:
         objs = list(ex.map(lambda s: _compile(s, obj_dir, defines), SOURCES))
     tmp = out + ".tmp%d" % os.getpid()
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs

@@ -186,6 +186,31 @@ pa_status pa_reshape_and_cache(const void *k, const void *v, void *k_cache, void
     return e == hipSuccess ? ok() : hip_fail(e, "reshape_and_cache launch");
 }
 
+pa_status pa_copy_blocks(void *k_cache, void *v_cache, const int64_t *block_pairs,
+                         int64_t num_pairs, const pa_shape *shape, void *stream)
+{
+    pa_status st = check_shape(shape, false);
+    if (st != PA_OK)
+        return st;
+    if (num_pairs < 0)
+        return fail(PA_ERR_INVALID, "num_pairs < 0");
+    if (num_pairs == 0)
+        return ok();
+    if (!k_cache || !v_cache || !block_pairs)
+        return fail(PA_ERR_INVALID, "NULL data pointer");
+    pa::CopyArgs a;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.block_pairs = block_pairs;
+    a.num_pairs = num_pairs;
+    a.num_blocks = shape->num_blocks;
+    a.block_bytes = (int64_t)16 * shape->num_kv_heads * shape->head_dim *
+                    (shape->cache_dtype == PA_F32 ? 4 : shape->cache_dtype == PA_BF16 ? 2 : 1);
+    a.pieces = pa::copy_pieces(a.block_bytes);
+    hipError_t e = pa::launch_copy_blocks(a, (hipStream_t)stream);
+    return e == hipSuccess ? ok() : hip_fail(e, "copy_blocks launch");
+}
+
 size_t pa_decode_workspace_bytes(const pa_shape *shape)
 {
     if (check_shape(shape, true) != PA_OK)

@@ -20,6 +20,18 @@ struct ReshapeArgs {
 };
 hipError_t launch_reshape_and_cache(const ReshapeArgs &a, hipStream_t stream);
 
+struct CopyArgs {
+    void *k_cache, *v_cache;
+    const int64_t *block_pairs;  // [num_pairs][2] (src, dst)
+    int64_t num_pairs;
+    int64_t num_blocks;
+    int64_t block_bytes;         // 16 * Hkv * head_dim * element bytes
+    int64_t pieces;              // copy_pieces(block_bytes)
+};
+// 16 KiB pieces (one work-group each) of one block of one pool
+int64_t copy_pieces(int64_t block_bytes);
+hipError_t launch_copy_blocks(const CopyArgs &a, hipStream_t stream);
+
 struct DecodeArgs {
     float *out;
     const void *q;

@@ -33,6 +33,7 @@ from typing import Dict, List, Optional
 import numpy as np
 import torch
 
+from . import binding
 from .block_manager import BLOCK_SIZE, BlockPool, SeqTable, pack_tables
 
 _TORCH_DT = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.float8_e4m3fn}
@@ -294,10 +295,12 @@ def make_step(cfg: Config, device="cuda", plan: Optional[HostPlan] = None) -> St
 
 
 def apply_cow(step: Step) -> None:
-    """Perform the plan's copy-on-write block copies on the device pools."""
-    for src, dst in step.plan.cow:
-        step.k_cache[dst].copy_(step.k_cache[src])
-        step.v_cache[dst].copy_(step.v_cache[src])
+    """Perform the plan's copy-on-write block copies on the device pools, all
+    in one pa_copy_blocks launch."""
+    if not step.plan.cow:
+        return
+    pairs = torch.tensor(step.plan.cow, dtype=torch.int64, device=step.k_cache.device)
+    binding.copy_blocks(step.k_cache, step.v_cache, pairs)
 
 
 def kv_bytes_per_token(cfg: Config) -> int:

@@ -119,6 +119,19 @@ def test_prefill_rejects_bad_arguments():
                                 P, 16, None) == binding.PA_ERR_WORKSPACE
 
 
+def test_copy_blocks_rejects_bad_arguments():
+    lib = binding.load()
+    P = FAKE
+    assert lib.pa_copy_blocks(P, P, P, -1, ctypes.byref(_shape()), None) == binding.PA_ERR_INVALID
+    assert lib.pa_copy_blocks(None, P, P, 3, ctypes.byref(_shape()), None) == binding.PA_ERR_INVALID
+    assert lib.pa_copy_blocks(P, P, None, 3, ctypes.byref(_shape()), None) == binding.PA_ERR_INVALID
+    assert lib.pa_copy_blocks(P, P, P, 3, None, None) == binding.PA_ERR_INVALID
+    assert (lib.pa_copy_blocks(P, P, P, 3, ctypes.byref(_shape(head_dim=96)), None) ==
+            binding.PA_ERR_UNSUPPORTED)
+    # nothing to copy: no pointer is touched
+    assert lib.pa_copy_blocks(None, None, None, 0, ctypes.byref(_shape()), None) == binding.PA_OK
+
+
 def test_status_strings():
     lib = binding.load()
     for s in range(5):

@@ -299,6 +299,34 @@ def test_partitions_of_many_short_sequences():
 
 
 # ----------------------------------------------------------------------------
+# copy-on-write block copies: bit-exact against the oracle's copy
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("storage,hkv,d", [("bf16", 8, 128), ("fp8", 40, 128), ("f32", 2, 64)])
+def test_copy_blocks_bit_exact(storage, hkv, d):
+    nblk = 300
+    tdt = {"bf16": torch.bfloat16, "fp8": torch.float8_e4m3fn, "f32": torch.float32}[storage]
+    g = torch.Generator(device="cuda")
+    g.manual_seed(41)
+    k = torch.randint(0, 256, (nblk, 16, hkv, d * tdt.itemsize), dtype=torch.uint8, device="cuda",
+                      generator=g).view(tdt)
+    v = torch.randint(0, 256, (nblk, 16, hkv, d * tdt.itemsize), dtype=torch.uint8, device="cuda",
+                      generator=g).view(tdt)
+    rng = np.random.default_rng(42)
+    perm = rng.permutation(nblk)
+    dst, src = perm[:100], rng.choice(perm[100:], 100)  # distinct destinations, never a source
+    pairs = np.stack([src, dst], 1).astype(np.int64)
+    pairs = np.concatenate([pairs, [[5, nblk], [-3, 7]]])  # outside the pool: skipped
+    kh = k.view(torch.uint8).cpu().numpy().reshape(nblk * 16, hkv, -1).copy()
+    vh = v.view(torch.uint8).cpu().numpy().reshape(nblk * 16, hkv, -1).copy()
+    oracle.copy_blocks(kh, vh, pairs)
+    binding.copy_blocks(k, v, torch.from_numpy(pairs).cuda())
+    torch.cuda.synchronize()
+    assert np.array_equal(k.view(torch.uint8).cpu().numpy().reshape(kh.shape), kh)
+    assert np.array_equal(v.view(torch.uint8).cpu().numpy().reshape(vh.shape), vh)
+
+
+# ----------------------------------------------------------------------------
 # chunked prefill special cases
 # ----------------------------------------------------------------------------
 
