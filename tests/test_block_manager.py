@@ -6,7 +6,8 @@ import numpy as np
 import pytest
 
 from paged_kv_cache_157_amd.block_manager import (BLOCK_SIZE, BlockPool, PoolExhausted,
-                                                   RefCountError, SeqTable, pack_tables, slot_of)
+                                                   RefCountError, SeqTable, block_hash,
+                                                   pack_tables, slot_of)
 from paged_kv_cache_157_amd.workload import CONFIGS, plan_step, scaled
 
 GOLDEN = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "worked_examples.json")))
@@ -185,3 +186,161 @@ def test_scaled_config_keeps_recipe():
     assert len(plan.context_lens) == 5
     bt2 = pack_tables(plan.tables, small.width)
     assert np.array_equal(bt2, plan.block_tables)
+
+
+# ----------------------------------------------------------------------------
+# prefix caching: block states, chained hashes, O(1) unlink from the queue
+# ----------------------------------------------------------------------------
+
+def _check_pool(p: BlockPool):
+    """The [VM] §3.5 invariants: queue = blocks with ref_cnt 0; a cached block
+    is one with ref_cnt 0 and a hash; every hash maps to the block holding it."""
+    q = p.free_blocks()
+    assert len(q) == len(set(q)) == p.num_free
+    refs = p.ref_counts()
+    assert set(q) == {b for b in range(p.num_blocks) if refs[b] == 0}
+    for h, b in p._cached.items():
+        assert p._hash[b] == h
+    for b in range(p.num_blocks):
+        assert p.state(b) == ("owned" if refs[b] > 0 else "cached" if p._hash[b] else "free")
+
+
+def test_block_life_cycle_states():
+    """[VM] §2: free -> owned (allocate), owned -> cached (release with a
+    hash), owned -> free (release without), cached -> owned (prefix hit),
+    cached -> free -> owned (evicted by an allocation)."""
+    p = BlockPool(4)
+    ids = list(range(40))
+    t, hit = SeqTable.allocate_cached(p, ids)  # 2 full blocks + 8 tokens
+    assert hit == 0 and [p.state(b) for b in t.blocks] == ["owned"] * 3
+    t.cache_full_blocks()
+    full, part = t.blocks[:2], t.blocks[2]
+    t.release()
+    assert [p.state(b) for b in full] == ["cached", "cached"] and p.state(part) == "free"
+    assert p.free_blocks() == [3] + full + [part]
+    u, hit = SeqTable.allocate_cached(p, ids[:32] + [99] * 5)
+    assert hit == 32 and u.blocks[:2] == full  # a hit: the cached blocks are owned again
+    assert p.state(full[0]) == "owned" and p.free_blocks() == [part]
+    _check_pool(p)
+    u.release()
+    v = SeqTable.allocate(p, 64)  # takes part, then the two cached blocks: evicted
+    assert v.blocks == [part, full[0], full[1], 3]
+    assert p.lookup(block_hash(None, ids[:16])) is None
+    _check_pool(p)
+
+
+def test_prefix_hit_unlinks_from_the_middle():
+    """[L33] §6.3: a hit takes a cached block out of the middle of the free
+    queue; every other block keeps its place in the eviction order."""
+    p = BlockPool(8)
+    a, _ = SeqTable.allocate_cached(p, list(range(16)))
+    b = SeqTable.allocate(p, 16)
+    c, _ = SeqTable.allocate_cached(p, list(range(100, 116)))
+    a.cache_full_blocks()
+    c.cache_full_blocks()
+    ab, bb, cb = a.blocks[0], b.blocks[0], c.blocks[0]
+    for t in (c, a, b):
+        t.release()
+    order = p.free_blocks()
+    assert order == [3, 4, 5, 6, 7, cb, ab, bb]  # c's cached block sits in the middle
+    target = p.lookup(block_hash(None, list(range(100, 116))))
+    assert target == cb
+    t, hit = SeqTable.allocate_cached(p, list(range(100, 116)) + [7])
+    assert hit == 16 and t.blocks[0] == target
+    assert p.free_blocks() == [x for x in order if x not in t.blocks]
+    _check_pool(p)
+
+
+def test_chained_hash_depends_on_the_prefix():
+    blk = list(range(16))
+    h1 = block_hash(None, blk)
+    assert h1 == block_hash(None, list(blk))
+    assert block_hash(h1, blk) != h1  # the same tokens one block later
+    assert block_hash(block_hash(None, [5] * 16), blk) != block_hash(None, blk)
+    p = BlockPool(16)
+    a, _ = SeqTable.allocate_cached(p, list(range(48)))
+    a.cache_full_blocks()
+    # same second block of tokens after a different first block: no hit
+    b, hit = SeqTable.allocate_cached(p, [7] * 16 + list(range(16, 48)))
+    assert hit == 0
+    # diverging inside the second block: only the first block hits
+    c, hit = SeqTable.allocate_cached(p, list(range(20)) + [-1] * 28)
+    assert hit == 16 and c.blocks[0] == a.blocks[0] and c.blocks[1] != a.blocks[1]
+    assert p.ref_cnt(a.blocks[0]) == 2
+    _check_pool(p)
+
+
+def test_fully_cached_prompt_still_computes_its_last_block():
+    p = BlockPool(8)
+    a, _ = SeqTable.allocate_cached(p, list(range(32)))
+    a.cache_full_blocks()
+    b, hit = SeqTable.allocate_cached(p, list(range(32)))
+    assert hit == 16 and b.blocks[0] == a.blocks[0] and b.blocks[1] != a.blocks[1]
+
+
+def test_system_prompt_reuse_example():
+    """[L33] §6.1-6.2: a 3,000-token system prompt, a 10-token question, the
+    answer, then a 10-token follow-up: the follow-up's prompt finds the first
+    turn's blocks and prefills only the tail (at least 99 % less)."""
+    g = GOLDEN["system_prompt_reuse"]
+    rng = np.random.default_rng(1)
+    system = [int(x) for x in rng.integers(0, 32000, g["system_prompt_tokens"])]
+    q1 = [int(x) for x in rng.integers(0, 32000, g["first_question_tokens"])]
+    answer = [int(x) for x in rng.integers(0, 32000, 50)]
+    q2 = [int(x) for x in rng.integers(0, 32000, g["follow_up_tokens"])]
+    p = BlockPool(1000, seed=3)
+    first, hit = SeqTable.allocate_cached(p, system + q1)
+    assert hit == 0
+    for tok in answer:  # decode: the answer's ids extend the table
+        first.append_token(tok)
+    first.cache_full_blocks()
+    first.release()  # the turn ends; its blocks stay cached
+    follow = system + q1 + answer + q2
+    second, hit = SeqTable.allocate_cached(p, follow)
+    assert hit == (len(system + q1 + answer) // BLOCK_SIZE) * BLOCK_SIZE
+    assert 1 - (len(follow) - hit) / len(follow) >= g["prefill_reduction_at_least"]
+    # another user with the same system prompt hits its full blocks only
+    other, hit2 = SeqTable.allocate_cached(p, system + [1, 2, 3])
+    assert hit2 == (len(system) // BLOCK_SIZE) * BLOCK_SIZE
+    assert other.blocks[:hit2 // 16] == second.blocks[:hit2 // 16]
+    _check_pool(p)
+
+
+def test_cached_allocation_that_does_not_fit_takes_nothing():
+    p = BlockPool(4)
+    a, _ = SeqTable.allocate_cached(p, list(range(32)))
+    a.cache_full_blocks()
+    a.release()
+    before = (p.free_blocks(), p.ref_counts())
+    with pytest.raises(PoolExhausted):
+        SeqTable.allocate_cached(p, list(range(32)) + list(range(100)))
+    assert p.free_blocks() == before[0] and np.array_equal(p.ref_counts(), before[1])
+
+
+def test_random_operations_keep_the_invariants():
+    rng = np.random.default_rng(9)
+    p = BlockPool(64, seed=4)
+    prompts = [[int(x) for x in rng.integers(0, 4, 16 * int(rng.integers(1, 5)))] for _ in range(6)]
+    live = []
+    for _ in range(400):
+        op = rng.integers(0, 4)
+        try:
+            if op == 0:
+                pr = prompts[int(rng.integers(0, 6))]
+                t, hit = SeqTable.allocate_cached(p, pr + [int(rng.integers(0, 4))])
+                assert hit % 16 == 0 and hit <= len(pr)
+                t.cache_full_blocks()
+                live.append(t)
+            elif op == 1 and live:
+                live.pop(int(rng.integers(0, len(live)))).release()
+            elif op == 2 and live:
+                live[int(rng.integers(0, len(live)))].append_token(int(rng.integers(0, 4)))
+            elif op == 3:
+                live.append(SeqTable.allocate(p, int(rng.integers(1, 40))))
+        except PoolExhausted:
+            pass
+        _check_pool(p)
+    refs = np.zeros(64, np.int64)
+    for t in live:
+        np.add.at(refs, np.array(t.blocks, dtype=np.int64), 1)
+    assert np.array_equal(refs, p.ref_counts())

@@ -355,6 +355,41 @@ def test_copy_on_write_fork_keeps_both_views():
     assert not np.array_equal(got_b, after_a)
 
 
+def test_prefix_cache_hit_leaves_the_output_unchanged():
+    """[VM] §3.4: a request that finds its prefix blocks cached reuses their KV
+    byte for byte, so its attention output equals that of a request that
+    recomputed and stored the whole prompt itself."""
+    from paged_kv_cache_157_amd.block_manager import BlockPool, SeqTable
+
+    rng = np.random.default_rng(13)
+    hkv, d = 2, 64
+    kp = np.zeros((32 * 16, hkv, d), np.uint16)
+    vp = np.zeros_like(kp)
+    # a row's KV is a function of the prefix up to it: here of its position
+    # and of the prompt it belongs to (equal prefixes, equal rows)
+    rows_k = to_bf16_bits(rng.standard_normal((60, hkv, d)).astype(np.float32))
+    rows_v = to_bf16_bits(rng.standard_normal((60, hkv, d)).astype(np.float32))
+    ids_a = [int(x) for x in rng.integers(0, 1000, 40)]
+    ids_b = ids_a[:35] + [int(x) for x in rng.integers(1000, 2000, 6)]
+    q = to_bf16_bits(rng.standard_normal((1, 4, d)).astype(np.float32))
+    pool = BlockPool(32, seed=2)
+    a, hit = SeqTable.allocate_cached(pool, ids_a)
+    oracle.reshape_and_cache(rows_k[:40], rows_v[:40], kp, vp, [a.slot(t) for t in range(40)])
+    a.cache_full_blocks()
+    a.release()
+    b, hit = SeqTable.allocate_cached(pool, ids_b)
+    assert hit == 32  # blocks 0 and 1; b diverges inside block 2
+    # b's own rows: the shared 35 tokens carry a's rows, the rest its own
+    bk = np.concatenate([rows_k[:35], rows_k[40:46]])
+    bv = np.concatenate([rows_v[:35], rows_v[40:46]])
+    oracle.reshape_and_cache(bk[hit:], bv[hit:], kp, vp, [b.slot(t) for t in range(hit, 41)])
+    got = oracle.decode(q, kp, vp, np.array([b.blocks], np.int32), np.array([41], np.int32), 0.125)
+    c = SeqTable.allocate(pool, 41)  # the same request without the cache
+    oracle.reshape_and_cache(bk, bv, kp, vp, [c.slot(t) for t in range(41)])
+    want = oracle.decode(q, kp, vp, np.array([c.blocks], np.int32), np.array([41], np.int32), 0.125)
+    assert np.array_equal(got, want)
+
+
 def test_copy_blocks_skips_ids_outside_the_pool():
     rng = np.random.default_rng(12)
     kp = rng.integers(0, 2 ** 16, (4 * 16, 2, 64), dtype=np.uint16)
