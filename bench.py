@@ -28,6 +28,7 @@ import numpy as np
 import torch
 
 from paged_kv_cache_157_amd import binding
+from paged_kv_cache_157_amd.replay import REPLAYS
 from paged_kv_cache_157_amd.workload import CONFIGS, apply_cow, kv_bytes_per_token, make_step
 
 HBM_PEAK_GBS = 8000.0
@@ -41,7 +42,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=300)
-    ap.add_argument("--workload", default="qwen7b", choices=sorted(CONFIGS))
+    ap.add_argument("--workload", default="qwen7b", choices=sorted(CONFIGS) + sorted(REPLAYS),
+                    help="a one-step workload, or a continuous-batching replay (replay_*)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB "
@@ -151,6 +153,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     binding.load()
+    if args.workload in REPLAYS:
+        replay_main(args)
+        return
     cfg = CONFIGS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -356,6 +361,31 @@ def main():
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(cfg, step)
     print(json.dumps(res), flush=True)
+
+
+def replay_main(args):
+    """A continuous-batching replay: every step schedules decodes and prefill
+    chunks under the token budget and runs the copy, cache-write, prefill and
+    decode kernels; the line reports the steady state in GPU time (HIP events
+    around each step's kernels) and the wall time including host scheduling."""
+    from paged_kv_cache_157_amd import replay
+
+    cfg = REPLAYS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    replay.run(cfg, dev, max_steps=min(args.warmup, 50))  # warms up the kernels and the allocator
+    r = replay.run(cfg, dev)
+    print(json.dumps({
+        "metric": "continuous-batching replay: tokens/s and decode KV GB/s in GPU time, 1 GPU",
+        "value": r["tokens_per_s_gpu"], "unit": "tokens/s", "n_gpus": 1,
+        "steps": r["steps"], "warmup": min(args.warmup, 50),
+        "ms_per_step": r["gpu_ms_per_step"], "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": cfg.cache_dtype, "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: {cfg.num_requests} requests, prompts U{list(cfg.prompt)}, "
+                               f"outputs U{list(cfg.output)}, budget {cfg.budget} tokens/step",
+                   "q_heads": cfg.num_q_heads, "kv_heads": cfg.num_kv_heads,
+                   "head_dim": cfg.head_dim, "pool_blocks": cfg.num_blocks, "seed": cfg.seed},
+        "replay": r}), flush=True)
 
 
 if __name__ == "__main__":

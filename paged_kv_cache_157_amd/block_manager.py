@@ -327,6 +327,27 @@ class SeqTable:
                     self.hashes.append(block_hash(parent, self.token_ids[-BLOCK_SIZE:]))
         return self.slot(pos), cow
 
+    def extend(self, n: int) -> Tuple[List[int], List[Tuple[int, int]]]:
+        """Reserve the slots of the next ``n`` tokens (a prefill chunk): the
+        first goes through ``append_token`` (copy-on-write of a shared last
+        block), the rest fill that block and then whole new blocks taken at
+        once.  Returns the slots and the copies to perform."""
+        if n <= 0:
+            return [], []
+        if self.token_ids is not None:
+            self.token_ids = None  # ids of the new tokens are not known
+        first, cow = self.append_token()
+        slots = [first]
+        pos = self.num_tokens
+        room = len(self.blocks) * BLOCK_SIZE - pos
+        rest = n - 1
+        if rest > room:
+            self.blocks += self.pool.allocate(-(-(rest - room) // BLOCK_SIZE))
+        for p in range(pos, pos + rest):
+            slots.append(slot_of(self.blocks, p))
+        self.num_tokens = pos + rest
+        return slots, [cow] if cow is not None else []
+
     def release(self) -> None:
         """The sequence finished: every block loses one reference (a cached
         block stays reusable until an allocation evicts it)."""

@@ -1,0 +1,209 @@
+"""Iteration-level scheduler with a unified token budget (host side).
+
+Every step re-forms the batch: requests that finished in the previous step
+have left and returned their blocks, and the step's budget of tokens is
+handed out first to the running decodes (one token each), then, in arrival
+order, to prompts that still need prefill, each taking
+min(tokens it still needs, budget left) as one chunk.  A prompt whose last
+chunk runs produces its first output token in that step and decodes from the
+next step on; a request leaves at the end of the step that produced its last
+output token.  The scheduler only plans: it emits slots, tables and lengths
+for the cache write, the chunked prefill and the decode, and the caller runs
+them.
+
+Sources, cited by page title and section:
+  [L33] "Lecture 33: KV Cache memory management -- PagedAttention, Continuous
+        Batching and Chunked Prefill": §3.2 (a finished request leaves at the
+        end of its step and a waiting one joins the next), §3.3 (blocks
+        returned by a finished request serve the next admission), §4.2 (a long
+        prompt runs as a series of chunks, each attending to the earlier ones
+        through the cache), §4.3 (one token budget for prefill and decode
+        alike), §4.4 (decodes first, one token each; the rest of the budget
+        cut into prefill chunks).
+  [VM]  "PagedAttention: managing the KV cache like virtual memory": §3.3
+        (blocks are taken as a sequence grows and returned when it ends).
+
+Preemption (swap or recompute) is out of scope: a decode that finds no free
+block raises PoolExhausted.  A prefill chunk is admitted only while one free
+block per running decode remains after it (so the decodes can grow);
+otherwise it waits, with every later prompt, for a later step.
+"""
+from __future__ import annotations
+
+from collections import deque
+from dataclasses import dataclass, field
+from typing import Deque, List, Optional, Tuple
+
+import numpy as np
+
+from .block_manager import BLOCK_SIZE, BlockPool, SeqTable
+
+
+@dataclass
+class Request:
+    """A request with a synthetic prompt length and output length (the token
+    at which it would emit end-of-sequence)."""
+    rid: int
+    prompt_len: int
+    output_len: int
+    table: Optional[SeqTable] = None
+    prefilled: int = 0    # prompt tokens whose KV is in the cache
+    generated: int = 0    # output tokens produced so far
+    first_step: int = -1  # step of the first chunk
+    done_step: int = -1   # step that produced the last output token
+
+    @property
+    def decoding(self) -> bool:
+        return self.prefilled == self.prompt_len and self.generated < self.output_len
+
+
+@dataclass
+class Chunk:
+    """One prefill chunk: prompt positions [start, start + n) of ``req``."""
+    req: Request
+    start: int
+    n: int
+    slots: List[int]
+
+
+@dataclass
+class StepPlan:
+    step: int
+    decodes: List[Request]
+    decode_slots: List[int]
+    chunks: List[Chunk]
+    cow: List[Tuple[int, int]] = field(default_factory=list)
+
+    @property
+    def num_tokens(self) -> int:
+        return len(self.decodes) + sum(c.n for c in self.chunks)
+
+    # ---- kernel inputs ---------------------------------------------------
+    def slot_mapping(self) -> np.ndarray:
+        """Slots of the step's new tokens: prefill chunks (request order, then
+        position), then one per decode."""
+        out = [s for c in self.chunks for s in c.slots] + list(self.decode_slots)
+        return np.asarray(out, dtype=np.int64)
+
+    def decode_inputs(self, width: int) -> Tuple[np.ndarray, np.ndarray]:
+        """[D, width] int32 tables (-1 padded) and [D] int32 context lengths of
+        the decodes; a decode attends every token up to its own."""
+        bt = np.full((len(self.decodes), width), -1, np.int32)
+        lens = np.zeros(len(self.decodes), np.int32)
+        for i, r in enumerate(self.decodes):
+            bt[i, :len(r.table.blocks)] = r.table.blocks
+            lens[i] = r.table.num_tokens
+        return bt, lens
+
+    def prefill_inputs(self, width: int) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+        """Tables, query_start ([R + 1]) and context lengths (chunk included)
+        of the chunks, in chunk order."""
+        bt = np.full((len(self.chunks), width), -1, np.int32)
+        qs = np.zeros(len(self.chunks) + 1, np.int32)
+        ctx = np.zeros(len(self.chunks), np.int32)
+        for i, c in enumerate(self.chunks):
+            bt[i, :len(c.req.table.blocks)] = c.req.table.blocks
+            qs[i + 1] = qs[i] + c.n
+            ctx[i] = c.start + c.n
+        return bt, qs, ctx
+
+
+class Scheduler:
+    """Admits, grows and retires requests under a per-step token budget."""
+
+    def __init__(self, pool: BlockPool, budget: int = 2048, max_chunk: Optional[int] = None):
+        if budget <= 0:
+            raise ValueError("budget must be positive")
+        self.pool = pool
+        self.budget = int(budget)
+        self.max_chunk = max_chunk
+        self.waiting: Deque[Request] = deque()   # arrival order, prefill not finished
+        self.running: List[Request] = []         # decoding
+        self.finished: List[Request] = []
+        self.step_no = 0
+
+    def add(self, req: Request) -> None:
+        if req.prompt_len <= 0 or req.output_len <= 0:
+            raise ValueError("prompt and output lengths must be positive")
+        self.waiting.append(req)
+
+    @property
+    def idle(self) -> bool:
+        return not self.waiting and not self.running
+
+    def schedule(self) -> StepPlan:
+        """Plan one step ([L33] §4.4)."""
+        left = self.budget
+        plan = StepPlan(self.step_no, [], [], [])
+        # phase 1: every running decode gets one token (its newest token's KV
+        # is written and it attends everything up to it)
+        for r in self.running:
+            if left == 0:
+                break
+            slot, cow = r.table.append_token()
+            if cow is not None:
+                plan.cow.append(cow)
+            plan.decodes.append(r)
+            plan.decode_slots.append(slot)
+            left -= 1
+        # phase 2: prefill chunks in arrival order from what is left
+        for r in self.waiting:
+            if left == 0:
+                break
+            need = r.prompt_len - r.prefilled
+            n = min(need, left)
+            if self.max_chunk is not None:
+                n = min(n, self.max_chunk)
+            if r.table is None:
+                r.table = SeqTable(self.pool)
+            have = len(r.table.blocks) * BLOCK_SIZE - r.table.num_tokens
+            new_blocks = -(-max(0, n - have) // BLOCK_SIZE)
+            # keep one free block per running decode, so that every decode
+            # can still grow by a block in the next step
+            if new_blocks > self.pool.num_free - len(self.running):
+                break  # no room: this prompt and every later one wait
+            slots, cows = r.table.extend(n)
+            plan.cow += cows
+            if r.first_step < 0:
+                r.first_step = self.step_no
+            plan.chunks.append(Chunk(r, r.prefilled, n, slots))
+            left -= n
+        return plan
+
+    def complete(self, plan: StepPlan) -> List[Request]:
+        """Account for a step that ran: prompts whose last chunk ran produce
+        their first output token and start decoding; every decode produces
+        one token; requests that produced their last token leave and return
+        their blocks ([L33] §3.2).  Returns the requests that finished."""
+        done = []
+        for c in plan.chunks:
+            r = c.req
+            r.prefilled += c.n
+            if r.prefilled == r.prompt_len:
+                r.generated = 1
+                self.waiting.remove(r)
+                if r.generated == r.output_len:
+                    done.append(r)
+                else:
+                    self.running.append(r)
+        for r in plan.decodes:
+            r.generated += 1
+            if r.generated == r.output_len:
+                done.append(r)
+                self.running.remove(r)
+        for r in done:
+            r.done_step = self.step_no
+            r.table.release()
+            self.finished.append(r)
+        self.step_no += 1
+        return done
+
+
+def synthetic_requests(n: int, seed: int, prompt: Tuple[int, int] = (64, 3000),
+                       output: Tuple[int, int] = (16, 256)) -> List[Request]:
+    """``n`` requests with prompt and output lengths drawn uniformly from the
+    given closed ranges (seeded); no token ids: lengths stand in for EOS."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    p = rng.integers(prompt[0], prompt[1], size=n, endpoint=True)
+    o = rng.integers(output[0], output[1], size=n, endpoint=True)
+    return [Request(i, int(a), int(b)) for i, (a, b) in enumerate(zip(p, o))]

@@ -344,3 +344,20 @@ def test_random_operations_keep_the_invariants():
     for t in live:
         np.add.at(refs, np.array(t.blocks, dtype=np.int64), 1)
     assert np.array_equal(refs, p.ref_counts())
+
+
+def test_extend_matches_token_by_token_growth():
+    for start, n in [(0, 1), (0, 16), (5, 11), (5, 12), (16, 40), (30, 100)]:
+        a_pool, b_pool = BlockPool(64, seed=2), BlockPool(64, seed=2)
+        a, b = SeqTable.allocate(a_pool, start), SeqTable.allocate(b_pool, start)
+        slots, cows = a.extend(n)
+        want = [b.append_token()[0] for _ in range(n)]
+        assert slots == want and cows == [] and a.blocks == b.blocks
+        assert a.num_tokens == b.num_tokens == start + n and a.waste() < BLOCK_SIZE
+    # a shared, partly filled last block is copied first
+    pool = BlockPool(16)
+    a = SeqTable.allocate(pool, 20)
+    b = SeqTable.with_prefix(pool, list(a.blocks), 20)
+    slots, cows = b.extend(30)
+    assert len(cows) == 1 and cows[0][0] == a.blocks[1] and b.blocks[1] == cows[0][1]
+    assert slots[0] == b.blocks[1] * 16 + 4 and len(b.blocks) == 4
