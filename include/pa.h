@@ -113,6 +113,29 @@ pa_status pa_reshape_and_cache(const void *k, const void *v, void *k_cache, void
 pa_status pa_copy_blocks(void *k_cache, void *v_cache, const int64_t *block_pairs,
                          int64_t num_pairs, const pa_shape *shape, void *stream);
 
+/*
+ * pa_swap_blocks -- move whole KV blocks between pools in different memories.
+ *   [L33] §5.2: a preempted request's blocks are copied over PCIe to host
+ *   memory, its device blocks freed, and copied back into free device blocks
+ *   when it resumes ([L33] §5.4 prices a round trip at
+ *   2 * S * KV_token / B_pcie).  One launch moves every pair; the GPU reads
+ *   or writes host memory directly.
+ *   src_k, src_v:  source pools, [src_num_blocks, 16, num_kv_heads, head_dim]
+ *   dst_k, dst_v:  destination pools, [dst_num_blocks, 16, num_kv_heads, head_dim]
+ *   block_pairs:   [num_pairs, 2] int64 (src, dst) block ids
+ *   Every pointer must be device memory of the current device or pinned
+ *   host memory (hipHostMalloc; torch's pin_memory); anything else gives
+ *   PA_ERR_INVALID before any launch.  Pairs with an id outside its pool
+ *   are skipped; dst ids must be distinct (the copies run concurrently).
+ *   Pinned host buffers must stay allocated until the stream has finished
+ *   the call.  The shape is validated as for pa_reshape_and_cache; its
+ *   num_kv_heads, head_dim and cache_dtype give the block size.
+ */
+pa_status pa_swap_blocks(const void *src_k, const void *src_v, int64_t src_num_blocks,
+                         void *dst_k, void *dst_v, int64_t dst_num_blocks,
+                         const int64_t *block_pairs, int64_t num_pairs, const pa_shape *shape,
+                         void *stream);
+
 /* Workspace bytes pa_decode needs for this shape (depends on the shape and
  * on the device's compute-unit count only). */
 size_t pa_decode_workspace_bytes(const pa_shape *shape);

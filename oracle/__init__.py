@@ -52,6 +52,8 @@ def _load():
         lib.oracle_reshape_and_cache.restype = None
         lib.oracle_copy_blocks.argtypes = [P, P, P, i64, i64, i64]
         lib.oracle_copy_blocks.restype = None
+        lib.oracle_swap_blocks.argtypes = [P, P, i64, P, P, i64, P, i64, i64]
+        lib.oracle_swap_blocks.restype = None
         lib.oracle_decode.argtypes = [P, P, ctypes.c_int, P, P, ctypes.c_int, dbl, P, i32, P,
                                       ctypes.c_int, ctypes.c_int, ctypes.c_int, dbl, P, P, i64,
                                       ctypes.c_int]
@@ -117,6 +119,19 @@ def copy_blocks(k_cache, v_cache, pairs) -> None:
     block_bytes = 16 * k_cache.shape[1] * k_cache.shape[2] * k_cache.itemsize
     _load().oracle_copy_blocks(_ptr(k_cache), _ptr(v_cache), _ptr(pairs), pairs.shape[0],
                                k_cache.shape[0] // 16, block_bytes)
+
+
+def swap_blocks(src_k, src_v, dst_k, dst_v, pairs) -> None:
+    """Block moves between two host pool pairs ([slots, Hkv, d], 16 slots per
+    block): for each (src, dst) row of ``pairs``, in order, block dst of the
+    destination pools becomes a copy of block src of the source pools."""
+    pairs = np.ascontiguousarray(np.asarray(pairs, dtype=np.int64).reshape(-1, 2))
+    assert src_k.shape[1:] == dst_k.shape[1:] and src_k.dtype == dst_k.dtype
+    assert src_v.shape == src_k.shape and dst_v.shape == dst_k.shape
+    block_bytes = 16 * src_k.shape[1] * src_k.shape[2] * src_k.itemsize
+    _load().oracle_swap_blocks(_ptr(src_k), _ptr(src_v), src_k.shape[0] // 16, _ptr(dst_k),
+                               _ptr(dst_v), dst_k.shape[0] // 16, _ptr(pairs), pairs.shape[0],
+                               block_bytes)
 
 
 def decode(q, k_cache, v_cache, block_tables, context_lens, scale, kv_scale=1.0,

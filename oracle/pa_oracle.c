@@ -189,6 +189,25 @@ void oracle_copy_blocks(void *k_cache, void *v_cache, const int64_t *pairs, int6
     }
 }
 
+/* Swapping ([L33] §5.2): for every (src, dst) pair, in order, block src of
+ * the source pools is copied over block dst of the destination pools (two
+ * separate pools of the same row layout).  Pairs naming a block outside
+ * its pool are skipped. */
+void oracle_swap_blocks(const void *src_k, const void *src_v, int64_t src_blocks, void *dst_k,
+                        void *dst_v, int64_t dst_blocks, const int64_t *pairs, int64_t num_pairs,
+                        int64_t block_bytes)
+{
+    for (int64_t p = 0; p < num_pairs; ++p) {
+        int64_t src = pairs[2 * p], dst = pairs[2 * p + 1];
+        if (src < 0 || src >= src_blocks || dst < 0 || dst >= dst_blocks)
+            continue;
+        memcpy((char *)dst_k + dst * block_bytes, (const char *)src_k + src * block_bytes,
+               (size_t)block_bytes);
+        memcpy((char *)dst_v + dst * block_bytes, (const char *)src_v + src * block_bytes,
+               (size_t)block_bytes);
+    }
+}
+
 /* ------------------------------------------------------------------ */
 /* Attention over a paged history                                     */
 /* ------------------------------------------------------------------ */

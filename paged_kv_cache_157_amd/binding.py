@@ -69,6 +69,8 @@ def load() -> ctypes.CDLL:
         lib.pa_prefill_chunk.restype = ctypes.c_int
         lib.pa_copy_blocks.argtypes = [P, P, P, i64, S, P]
         lib.pa_copy_blocks.restype = ctypes.c_int
+        lib.pa_swap_blocks.argtypes = [P, P, i64, P, P, i64, P, i64, S, P]
+        lib.pa_swap_blocks.restype = ctypes.c_int
         lib.pa_status_string.argtypes = [ctypes.c_int]
         lib.pa_status_string.restype = ctypes.c_char_p
         lib.pa_last_error.argtypes = []
@@ -170,6 +172,38 @@ def copy_blocks(k_cache: torch.Tensor, v_cache: torch.Tensor, block_pairs: torch
     shape = make_shape(k_cache.shape[2], k_cache, q_dtype, 0, 1)
     _check(load().pa_copy_blocks(_ptr(k_cache), _ptr(v_cache), _ptr(block_pairs),
                                  block_pairs.shape[0], ctypes.byref(shape), _stream(dev)))
+
+
+def swap_blocks(src_k: torch.Tensor, src_v: torch.Tensor, dst_k: torch.Tensor,
+                dst_v: torch.Tensor, block_pairs: torch.Tensor,
+                device: Optional[torch.device] = None) -> None:
+    """pa_swap_blocks: dst[dst_id] = src[src_id] for every (src_id, dst_id) row of
+    block_pairs, between pools on the GPU and pools in pinned host memory (any
+    mix).  Runs on the current stream of ``device`` (default: the CUDA device of
+    whichever argument is on one, else the current device)."""
+    ts = (("src_k", src_k), ("src_v", src_v), ("dst_k", dst_k), ("dst_v", dst_v),
+          ("block_pairs", block_pairs))
+    for name, t in ts:
+        if not (t.is_cuda or t.is_pinned()):
+            raise ValueError(f"{name} must be a CUDA tensor or pinned host memory")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if device is None:
+        cuda = [t.device for _, t in ts if t.is_cuda]
+        device = cuda[0] if cuda else torch.device("cuda", torch.cuda.current_device())
+    if block_pairs.dtype != torch.int64 or block_pairs.dim() != 2 or block_pairs.shape[1] != 2:
+        raise ValueError("block_pairs must be [n, 2] int64 (src, dst)")
+    for a, b in ((src_k, src_v), (dst_k, dst_v)):
+        if a.shape != b.shape:
+            raise ValueError("the K and V pools of one side must match")
+    if (src_k.dtype != dst_k.dtype or src_v.dtype != dst_v.dtype or
+            tuple(src_k.shape[1:]) != tuple(dst_k.shape[1:])):
+        raise ValueError("source and destination pools differ in block layout or dtype")
+    q_dtype = torch.float32 if src_k.dtype == torch.float32 else torch.bfloat16
+    shape = make_shape(src_k.shape[2], src_k, q_dtype, 0, 1)
+    _check(load().pa_swap_blocks(_ptr(src_k), _ptr(src_v), src_k.shape[0], _ptr(dst_k),
+                                 _ptr(dst_v), dst_k.shape[0], _ptr(block_pairs),
+                                 block_pairs.shape[0], ctypes.byref(shape), _stream(device)))
 
 
 def decode_workspace_bytes(shape: PAShape) -> int:

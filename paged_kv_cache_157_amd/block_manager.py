@@ -18,6 +18,8 @@ Sources, cited by page title and section:
         §3.5 (the three block states: free, owned, cached-free).
   [L33] §6.3: the free queue is a doubly linked list so that a cached block
         can be taken out of the middle of it in O(1) on a prefix hit.
+  [L33] §5.2, §5.4: preemption by swapping a request's blocks to host memory
+        and back; the cost of a round trip is 2 * S * KV_token / B_pcie.
 
 Differences from the pages' own sketches:
   - The free queue starts as a seeded permutation of the block ids, so that
@@ -360,6 +362,37 @@ class SeqTable:
     def waste(self) -> int:
         """Reserved but unused token slots (always < one block)."""
         return len(self.blocks) * BLOCK_SIZE - self.num_tokens
+
+
+def swap_out(table: SeqTable, host: BlockPool) -> List[Tuple[int, int]]:
+    """Preemption by swapping ([L33] §5.2): the table's blocks get blocks of
+    the host pool, the device blocks lose this table's reference (a block
+    another table shares stays on the device for it), and the table now
+    points into the host pool.  Returns the (device, host) block copies to
+    run before the freed device blocks are reused."""
+    hb = host.allocate(len(table.blocks))
+    pairs = list(zip(table.blocks, hb))
+    table.pool.free(table.blocks)
+    table.pool, table.blocks = host, hb
+    return pairs
+
+
+def swap_in(table: SeqTable, device: BlockPool) -> List[Tuple[int, int]]:
+    """Resume a swapped-out table: it gets fresh device blocks (private ones,
+    even where its blocks were shared before) and gives its host blocks back.
+    Returns the (host, device) block copies to run before it is scheduled."""
+    db = device.allocate(len(table.blocks))
+    pairs = list(zip(table.blocks, db))
+    table.pool.free(table.blocks)
+    table.pool, table.blocks = device, db
+    table.hashes = []  # the new blocks are not registered as cached prefixes
+    return pairs
+
+
+def swap_time_model(tokens: int, kv_bytes_per_token: int, link_bytes_per_s: float) -> float:
+    """Seconds to swap ``tokens`` tokens out and back in over a host link
+    ([L33] §5.4): 2 * S * KV_token / B_pcie."""
+    return 2.0 * tokens * kv_bytes_per_token / link_bytes_per_s
 
 
 def pack_tables(tables: List[SeqTable], width: int, pad: int = -1) -> np.ndarray:

@@ -1,6 +1,9 @@
-// copy_blocks.hip -- copy whole KV blocks inside the pools: the device half
-// of copy-on-write ("Lecture 33" §2.4: a sequence that writes into a block
-// other sequences still reference first gets a private copy of it).
+// copy_blocks.hip -- copy whole KV blocks between pools: inside the device
+// pools, the device half of copy-on-write ("Lecture 33" §2.4: a sequence that
+// writes into a block other sequences still reference first gets a private
+// copy of it); between the device pools and pools in pinned host memory,
+// swapping a preempted request's blocks out and back in ("Lecture 33" §5.2:
+// the blocks cross PCIe to host memory and return when there is room).
 //
 // A work-group copies one 16 KiB piece of one block of one pool (K or V) at
 // a time: every thread moves four 16-byte words, all loads issued before any
@@ -28,12 +31,13 @@ __global__ __launch_bounds__(kCopyThreads) void copy_blocks_kernel(CopyArgs a)
         const int side = r >= a.pieces;  // 0: K pool, 1: V pool
         const int64_t piece = side ? r - a.pieces : r;
         const int64_t src = pairs[2 * p], dst = pairs[2 * p + 1];
-        if (src < 0 || src >= a.num_blocks || dst < 0 || dst >= a.num_blocks)
-            continue;  // pairs naming a block outside the pool are skipped
-        char *pool = (char *)(side ? a.v_cache : a.k_cache);
+        if (src < 0 || src >= a.src_blocks || dst < 0 || dst >= a.dst_blocks)
+            continue;  // pairs naming a block outside its pool are skipped
+        const char *sp = (const char *)(side ? a.src_v : a.src_k);
+        char *dp = (char *)(side ? a.dst_v : a.dst_k);
         const int64_t off = piece * kCopyPiece;
-        const u32x4 *s = (const u32x4 *)(pool + src * a.block_bytes + off);
-        u32x4 *d = (u32x4 *)(pool + dst * a.block_bytes + off);
+        const u32x4 *s = (const u32x4 *)(sp + src * a.block_bytes + off);
+        u32x4 *d = (u32x4 *)(dp + dst * a.block_bytes + off);
         const int64_t words = (a.block_bytes - off) / 16;  // this block's words from the piece on
         u32x4 t[kCopyWords];
 #pragma unroll

@@ -82,6 +82,34 @@ int decode_grid(const pa_shape *s)
     return slot;
 }
 
+// Bytes of one block of one pool: 16 token rows of num_kv_heads x head_dim.
+int64_t block_bytes_of(const pa_shape *s)
+{
+    return (int64_t)16 * s->num_kv_heads * s->head_dim *
+           (s->cache_dtype == PA_F32 ? 4 : s->cache_dtype == PA_BF16 ? 2 : 1);
+}
+
+// The address a kernel uses for p: device memory as it is, pinned host memory
+// through the device mapping the runtime reports; false for anything else
+// (pageable host memory, which a kernel cannot reach).
+bool device_address(const void *p, const void **out)
+{
+    hipPointerAttribute_t at;
+    if (hipPointerGetAttributes(&at, p) != hipSuccess) {
+        (void)hipGetLastError();  // not an error of the next call
+        return false;
+    }
+    if (at.type == hipMemoryTypeDevice) {
+        *out = p;
+        return true;
+    }
+    if (at.type == hipMemoryTypeHost && at.devicePointer && at.hostPointer) {
+        *out = (const char *)at.devicePointer + ((const char *)p - (const char *)at.hostPointer);
+        return true;
+    }
+    return false;
+}
+
 pa_status check_shape(const pa_shape *s, bool need_tables)
 {
     if (!s)
@@ -199,16 +227,53 @@ pa_status pa_copy_blocks(void *k_cache, void *v_cache, const int64_t *block_pair
     if (!k_cache || !v_cache || !block_pairs)
         return fail(PA_ERR_INVALID, "NULL data pointer");
     pa::CopyArgs a;
-    a.k_cache = k_cache;
-    a.v_cache = v_cache;
+    a.src_k = k_cache;
+    a.src_v = v_cache;
+    a.dst_k = k_cache;
+    a.dst_v = v_cache;
     a.block_pairs = block_pairs;
     a.num_pairs = num_pairs;
-    a.num_blocks = shape->num_blocks;
-    a.block_bytes = (int64_t)16 * shape->num_kv_heads * shape->head_dim *
-                    (shape->cache_dtype == PA_F32 ? 4 : shape->cache_dtype == PA_BF16 ? 2 : 1);
+    a.src_blocks = a.dst_blocks = shape->num_blocks;
+    a.block_bytes = block_bytes_of(shape);
     a.pieces = pa::copy_pieces(a.block_bytes);
     hipError_t e = pa::launch_copy_blocks(a, (hipStream_t)stream);
     return e == hipSuccess ? ok() : hip_fail(e, "copy_blocks launch");
+}
+
+pa_status pa_swap_blocks(const void *src_k, const void *src_v, int64_t src_num_blocks, void *dst_k,
+                         void *dst_v, int64_t dst_num_blocks, const int64_t *block_pairs,
+                         int64_t num_pairs, const pa_shape *shape, void *stream)
+{
+    pa_status st = check_shape(shape, false);
+    if (st != PA_OK)
+        return st;
+    if (num_pairs < 0 || src_num_blocks < 0 || dst_num_blocks < 0)
+        return fail(PA_ERR_INVALID, "negative count");
+    if (num_pairs == 0)
+        return ok();
+    if (!src_k || !src_v || !dst_k || !dst_v || !block_pairs)
+        return fail(PA_ERR_INVALID, "NULL data pointer");
+    // every pointer the kernel uses: device memory, or pinned host memory
+    // through its device mapping
+    const void *ptrs[5] = {src_k, src_v, dst_k, dst_v, block_pairs};
+    const void *dev[5];
+    for (int i = 0; i < 5; ++i)
+        if (!device_address(ptrs[i], &dev[i]))
+            return fail(PA_ERR_INVALID,
+                        "pointer %d is neither device memory nor pinned host memory", i);
+    pa::CopyArgs a;
+    a.src_k = dev[0];
+    a.src_v = dev[1];
+    a.dst_k = (void *)dev[2];
+    a.dst_v = (void *)dev[3];
+    a.block_pairs = (const int64_t *)dev[4];
+    a.num_pairs = num_pairs;
+    a.src_blocks = src_num_blocks;
+    a.dst_blocks = dst_num_blocks;
+    a.block_bytes = block_bytes_of(shape);
+    a.pieces = pa::copy_pieces(a.block_bytes);
+    hipError_t e = pa::launch_copy_blocks(a, (hipStream_t)stream);
+    return e == hipSuccess ? ok() : hip_fail(e, "swap_blocks launch");
 }
 
 size_t pa_decode_workspace_bytes(const pa_shape *shape)

@@ -21,10 +21,11 @@ struct ReshapeArgs {
 hipError_t launch_reshape_and_cache(const ReshapeArgs &a, hipStream_t stream);
 
 struct CopyArgs {
-    void *k_cache, *v_cache;
+    const void *src_k, *src_v;   // pools read (device addresses)
+    void *dst_k, *dst_v;         // pools written (may be the same pools)
     const int64_t *block_pairs;  // [num_pairs][2] (src, dst)
     int64_t num_pairs;
-    int64_t num_blocks;
+    int64_t src_blocks, dst_blocks;  // blocks in the source / destination pools
     int64_t block_bytes;         // 16 * Hkv * head_dim * element bytes
     int64_t pieces;              // copy_pieces(block_bytes)
 };

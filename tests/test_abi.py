@@ -132,6 +132,16 @@ def test_copy_blocks_rejects_bad_arguments():
     assert lib.pa_copy_blocks(None, None, None, 0, ctypes.byref(_shape()), None) == binding.PA_OK
 
 
+def test_swap_blocks_rejects_bad_arguments():
+    lib = binding.load()
+    P, S = FAKE, ctypes.byref(_shape())
+    assert lib.pa_swap_blocks(P, P, 4, P, P, 4, P, -1, S, None) == binding.PA_ERR_INVALID
+    assert lib.pa_swap_blocks(P, P, -4, P, P, 4, P, 2, S, None) == binding.PA_ERR_INVALID
+    assert lib.pa_swap_blocks(P, None, 4, P, P, 4, P, 2, S, None) == binding.PA_ERR_INVALID
+    assert lib.pa_swap_blocks(P, P, 4, P, P, 4, P, 2, None, None) == binding.PA_ERR_INVALID
+    assert lib.pa_swap_blocks(None, None, 0, None, None, 0, None, 0, S, None) == binding.PA_OK
+
+
 def test_status_strings():
     lib = binding.load()
     for s in range(5):

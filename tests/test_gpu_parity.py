@@ -6,6 +6,7 @@ Small cases compare every output; full-size configurations compare a sample
 of (sequence, head) pairs that always includes the longest and shortest
 sequence.
 """
+import ctypes
 import math
 
 import numpy as np
@@ -324,6 +325,88 @@ def test_copy_blocks_bit_exact(storage, hkv, d):
     torch.cuda.synchronize()
     assert np.array_equal(k.view(torch.uint8).cpu().numpy().reshape(kh.shape), kh)
     assert np.array_equal(v.view(torch.uint8).cpu().numpy().reshape(vh.shape), vh)
+
+
+# ----------------------------------------------------------------------------
+# swapping blocks between the device pools and pools in pinned host memory
+# ----------------------------------------------------------------------------
+
+def _random_pools(nblk, hkv, d, tdt, seed, device):
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    mk = lambda: torch.randint(0, 256, (nblk, 16, hkv, d * tdt.itemsize), dtype=torch.uint8,
+                               device="cuda", generator=g).view(tdt).to(device)
+    return mk(), mk()
+
+
+def _bits(t):
+    return t.view(torch.uint8).cpu().numpy().reshape(t.shape[0] * 16, t.shape[2], -1).copy()
+
+
+@pytest.mark.parametrize("pairs_on_host", [False, True])
+@pytest.mark.parametrize("storage,hkv,d", [("bf16", 8, 128), ("fp8", 4, 128)])
+def test_swap_blocks_round_trip_bit_exact(storage, hkv, d, pairs_on_host):
+    tdt = {"bf16": torch.bfloat16, "fp8": torch.float8_e4m3fn}[storage]
+    k, v = _random_pools(300, hkv, d, tdt, 51, "cuda")
+    hk = torch.zeros((64, 16, hkv, d), dtype=tdt).pin_memory()
+    hv = torch.zeros_like(hk).pin_memory()
+    rng = np.random.default_rng(52)
+    dev_out = rng.permutation(300)[:40]
+    host_in = rng.permutation(64)[:40]
+    out_pairs = np.concatenate([np.stack([dev_out, host_in], 1), [[3, 64]]]).astype(np.int64)
+    kh, vh, hkh, hvh = _bits(k), _bits(v), _bits(hk), _bits(hv)
+    oracle.swap_blocks(kh, vh, hkh, hvh, out_pairs)
+    pt = torch.from_numpy(out_pairs)
+    pt = pt.pin_memory() if pairs_on_host else pt.cuda()
+    binding.swap_blocks(k, v, hk, hv, pt)
+    torch.cuda.synchronize()
+    assert np.array_equal(_bits(hk), hkh) and np.array_equal(_bits(hv), hvh)
+    # back into other device blocks
+    dev_back = rng.permutation(300)[:40]
+    in_pairs = np.stack([host_in, dev_back], 1).astype(np.int64)
+    oracle.swap_blocks(hkh, hvh, kh, vh, in_pairs)
+    pt = torch.from_numpy(in_pairs)
+    pt = pt.pin_memory() if pairs_on_host else pt.cuda()
+    binding.swap_blocks(hk, hv, k, v, pt)
+    torch.cuda.synchronize()
+    assert np.array_equal(_bits(k), kh) and np.array_equal(_bits(v), vh)
+
+
+def test_swap_blocks_rejects_pageable_host_memory():
+    k, v = _random_pools(8, 2, 64, torch.bfloat16, 53, "cuda")
+    pageable = np.zeros((8, 16, 2, 64), np.uint16)
+    pairs = torch.tensor([[0, 1]], dtype=torch.int64, device="cuda")
+    shape = binding.make_shape(2, k, torch.bfloat16, 0, 1)
+    P = ctypes.c_void_p(pageable.ctypes.data)
+    lib = binding.load()
+    st = lib.pa_swap_blocks(ctypes.c_void_p(k.data_ptr()), ctypes.c_void_p(v.data_ptr()), 8, P, P,
+                            8, ctypes.c_void_p(pairs.data_ptr()), 1, ctypes.byref(shape), None)
+    assert st == binding.PA_ERR_INVALID
+    # the check leaves no error behind for the next call
+    binding.copy_blocks(k, v, pairs)
+    torch.cuda.synchronize()
+
+
+def test_swap_round_trip_keeps_decode_bits():
+    """A preempted sequence comes back into different device blocks and
+    decodes to the same bits."""
+    lens = [700, 33, 1500]
+    p = random_problem(54, 3, 32, 8, 128, lens, 300, "bf16")
+    a = decode_problem(p)
+    hk = torch.zeros((300, 16, 8, 128), dtype=torch.bfloat16).pin_memory()
+    hv = torch.zeros_like(hk).pin_memory()
+    used = p["bt_h"][p["bt_h"] >= 0]
+    binding.swap_blocks(p["k"], p["v"], hk, hv,
+                        torch.from_numpy(np.stack([used, used], 1).astype(np.int64)).cuda())
+    rng = np.random.default_rng(55)
+    pi = rng.permutation(300)  # new device home of every block
+    p["k"].normal_()
+    p["v"].normal_()
+    binding.swap_blocks(hk, hv, p["k"], p["v"],
+                        torch.from_numpy(np.stack([used, pi[used]], 1).astype(np.int64)).cuda())
+    p2 = dict(p, bt=to_dev(np.where(p["bt_h"] >= 0, pi[np.maximum(p["bt_h"], 0)], -1)
+                            .astype(np.int32)))
+    assert np.array_equal(decode_problem(p2), a)
 
 
 # ----------------------------------------------------------------------------
