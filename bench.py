@@ -7,14 +7,18 @@ new tokens (pa_reshape_and_cache), the decode attention of every sequence
 (pa_prefill_chunk).  Inputs are seeded synthetic tensors already resident in
 HBM before the timed region.
 
-    python bench.py [--steps K] [--warmup W] [--workload qwen7b] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--workload qwen7b] [--no-cpu-baseline] [--extras]
+    python bench.py --workload replay_qwen7b
 
 Prints one JSON line.  `value` is the effective KV bandwidth of the step: KV
 bytes the decode must read (each sequence's K and V rows, once) divided by
-the step time.  The roofline entry is for the decode launch (its two
-kernels), timed with HIP events on the stream the kernels run on, in a
-second pass right after the timed steps.  The cache write, shorter than one
-host submission, is timed over 200 launches queued behind a GPU-side wait.
+the step time.  The roofline entry is for the decode launch (one kernel),
+timed with HIP events on the stream the kernel runs on, in a second pass
+right after the timed steps.  The cache write, shorter than one host
+submission, is timed over 200 launches queued behind a GPU-side wait.
+``--extras`` adds the decode with the Infinity Cache evicted, a plain device
+copy, and the block copy and swap kernels.  A replay_* workload runs the
+continuous-batching replay instead and reports its steady state.
 """
 from __future__ import annotations
 
@@ -45,6 +49,11 @@ def parse():
     ap.add_argument("--workload", default="qwen7b", choices=sorted(CONFIGS) + sorted(REPLAYS),
                     help="a one-step workload, or a continuous-batching replay (replay_*)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--extras", action="store_true",
+                    help="also measure the decode with the Infinity Cache evicted, a plain "
+                         "device copy, pa_copy_blocks and pa_swap_blocks (after the timed "
+                         "steps; off by default so that a profile of the default command "
+                         "holds the warm decode launches only)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB "
                          "(a known-size reference for hardware byte counters)")
@@ -64,6 +73,14 @@ def algorithmic_bytes(cfg, step) -> dict:
     out = cfg.num_seqs * cfg.num_q_heads * cfg.head_dim * 4
     tables = int(((L + 15) // 16).sum()) * 4 + 4 * cfg.num_seqs
     return dict(kv=kv, total=kv + q + out + tables)
+
+
+def decode_kernel_name(cfg) -> str:
+    """The kernel pa_decode runs for this shape: four KV heads per work-group
+    when there are at least two groups of four and G >= 2, else one."""
+    G = cfg.num_q_heads // cfg.num_kv_heads
+    hg = cfg.num_kv_heads % 4 == 0 and cfg.num_kv_heads >= 8 and G >= 2
+    return "pa::hg::decode_hg_kernel" if hg else "pa::decode_kernel"
 
 
 def unique_kv_bytes(cfg, step) -> int:
@@ -261,7 +278,7 @@ def main():
 
     # copy-on-write copies (pa_copy_blocks): up to 1024 pairs from blocks the
     # batch uses into free blocks, so no table's data changes
-    free = step.plan.pool.free_blocks()[:1024]
+    free = step.plan.pool.free_blocks()[:1024] if args.extras else []
     used = np.unique(step.plan.block_tables[step.plan.block_tables >= 0])
     copy_res = None
     if free and len(used):
@@ -306,20 +323,22 @@ def main():
                             swap_time_model(n * 16, kv_bytes_per_token(cfg), link) * 1e6, 1))
         del hk, hv, flat_d, flat_h
 
-    evict = torch.ones(192 << 20, dtype=torch.float32, device=dev)  # 768 MiB
-    dec_cold = cold_us(decode, evict)
-    del evict
-    # read-stream context: a plain 1 GiB device copy (reads and writes 1 GiB)
-    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-    dst = torch.empty_like(src)
-    dst.copy_(src)
-    e0.record()
-    for _ in range(5):
+    dec_cold = copy_gbs = None
+    if args.extras:
+        evict = torch.ones(192 << 20, dtype=torch.float32, device=dev)  # 768 MiB
+        dec_cold = cold_us(decode, evict)
+        del evict
+        # bandwidth context: a plain 1 GiB device copy (reads and writes 1 GiB)
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
         dst.copy_(src)
-    e1.record()
-    torch.cuda.synchronize()
-    copy_gbs = 2 * (1 << 30) * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e9
-    del src, dst
+        e0.record()
+        for _ in range(5):
+            dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        copy_gbs = round(2 * (1 << 30) * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
+        del src, dst
     if args.copy_probe_mib:
         # a plain device copy of known size: rocprofv3 --pmc reads of FETCH_SIZE /
         # WRITE_SIZE for it convert the counters into bytes
@@ -368,15 +387,16 @@ def main():
         "decode_us": round(dec_ms * 1e3, 2),
         # with the Infinity Cache evicted before every launch (decode_us: warm)
         "decode_cold_us": dec_cold,
-        "decode_cold_kv_gbs": round(ab["kv"] / (dec_cold["median"] * 1e-6) / 1e9, 2),
-        "device_copy_gbs": round(copy_gbs, 1),
+        "decode_cold_kv_gbs": (round(ab["kv"] / (dec_cold["median"] * 1e-6) / 1e9, 2)
+                               if dec_cold else None),
+        "device_copy_gbs": copy_gbs,
         "cache_write_us": round(cw_ms * 1e3, 2),
         "copy_blocks": copy_res,
         "swap_blocks": swap_res,
         "decode_kv_gbs": round(ab["kv"] / (dec_ms * 1e-3) / 1e9, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "kernel": "pa_decode (decode_kernel, one launch)",
+                     "traffic": traffic, "kernel": f"pa_decode ({decode_kernel_name(cfg)}, one launch)",
                      "algorithmic_bytes_per_launch": ab["total"]},
     }
     if uniq < ab["kv"]:  # shared blocks: the distinct bytes read as well
