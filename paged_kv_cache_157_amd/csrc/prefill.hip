@@ -24,11 +24,13 @@
 //   * S^T = K Q^T puts one query row per lane (column of the MFMA result),
 //     so the row maximum and sum are in-lane plus one exchange between the two
 //     half-waves.  Masks are applied only on tiles that cross the causal
-//     diagonal or the end of the context.  The probabilities are split into a
-//     bf16 head and a bf16 tail (together exact to about 2^-16) and both are
-//     multiplied with V on the matrix cores (O = P V); a single bf16 rounding
-//     of P would cost up to 2^-8 relative weight error, too coarse for rows
-//     with few keys.
+//     diagonal or the end of the context.  With a bf16 cache the
+//     probabilities are split into a bf16 head and a bf16 tail (together
+//     exact to about 2^-16) and both are multiplied with V on the matrix cores
+//     (O = P V): a single bf16 rounding of P costs up to 2^-8 relative weight
+//     error, too coarse for rows with few keys at that cache's precision.
+//     With an fp8 cache, whose values carry far coarser rounding, the head
+//     alone is used (half the P V products).
 //   * The running maximum is raised only when a tile exceeds it by more than
 //     8 (base 2); that rare path rescales the accumulators through LDS.
 //   * When the key range is split over several work-groups, each writes
@@ -418,20 +420,33 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
                 p[j] = fast_exp2(fmaf(s[kc][8 * h8 + j], c, -mu));
                 lsum += p[j];
             }
-            uint32_t h[4], t[4];
+            uint32_t h[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
+            for (int j = 0; j < 4; ++j)
                 h[j] = pack_bf16(p[2 * j], p[2 * j + 1]);
-                t[j] = pack_bf16(p[2 * j] - bf16_lo(h[j]), p[2 * j + 1] - bf16_hi(h[j]));
-            }
             const u32x4 ph = u32x4{h[0], h[1], h[2], h[3]};
-            const u32x4 pl = u32x4{t[0], t[1], t[2], t[3]};
+            if constexpr (CDT == DT_FP8) {
+                // fp8 KV: one bf16 rounding of P (2^-8 relative per weight) stays
+                // far inside that cache's tolerance, so no tail
 #pragma unroll
-            for (int dt = 0; dt < D / 32; ++dt) {
-                const u32x4 vb =
-                    u32x4{vr[2 * dt][0], vr[2 * dt][1], vr[2 * dt + 1][0], vr[2 * dt + 1][1]};
-                o[dt] = mfma32(ph, vb, o[dt]);
-                o[dt] = mfma32(pl, vb, o[dt]);
+                for (int dt = 0; dt < D / 32; ++dt) {
+                    const u32x4 vb =
+                        u32x4{vr[2 * dt][0], vr[2 * dt][1], vr[2 * dt + 1][0], vr[2 * dt + 1][1]};
+                    o[dt] = mfma32(ph, vb, o[dt]);
+                }
+            } else {
+                uint32_t t[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    t[j] = pack_bf16(p[2 * j] - bf16_lo(h[j]), p[2 * j + 1] - bf16_hi(h[j]));
+                const u32x4 pl = u32x4{t[0], t[1], t[2], t[3]};
+#pragma unroll
+                for (int dt = 0; dt < D / 32; ++dt) {
+                    const u32x4 vb =
+                        u32x4{vr[2 * dt][0], vr[2 * dt][1], vr[2 * dt + 1][0], vr[2 * dt + 1][1]};
+                    o[dt] = mfma32(ph, vb, o[dt]);
+                    o[dt] = mfma32(pl, vb, o[dt]);
+                }
             }
         });
     };
