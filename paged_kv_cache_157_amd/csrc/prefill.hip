@@ -398,8 +398,14 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
         // a row with no valid key yet keeps mref = -inf: its probabilities are 0
         return mref == -INFINITY ? 0.f : mref;
     };
-    // ---- probabilities (bf16 head + tail) and O += P V, four 16-key steps ----------
-    auto pv_tile = [&](const f32x16 (&s)[2], float mu, const char *vt_lds) {
+    // ---- probabilities and O += P V, four 16-key steps --------------------------------
+    // MODE 0 (bf16 caches): P as a bf16 head and a bf16 tail (weights exact to
+    // ~2^-16); 1 (fp8 caches): one bf16 rounding of P, and the rounded weights
+    // enter the row sum as they enter the products, so the result stays a
+    // convex combination of V rows (a row with one key returns its value
+    // exactly).
+    auto pv_tile = [&](const f32x16 (&s)[2], float mu, const char *vt_lds, auto mode_) {
+        constexpr int MODE = decltype(mode_)::value;
         static_for<4>([&](auto ks_) {
             constexpr int ks = decltype(ks_)::value;
             constexpr int kc = ks >> 1, h8 = ks & 1;
@@ -416,18 +422,16 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
             }
             float p[8];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
+            for (int j = 0; j < 8; ++j)
                 p[j] = fast_exp2(fmaf(s[kc][8 * h8 + j], c, -mu));
-                lsum += p[j];
-            }
             uint32_t h[4];
+            if constexpr (MODE == 1) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                h[j] = pack_bf16(p[2 * j], p[2 * j + 1]);
-            const u32x4 ph = u32x4{h[0], h[1], h[2], h[3]};
-            if constexpr (CDT == DT_FP8) {
-                // fp8 KV: one bf16 rounding of P (2^-8 relative per weight) stays
-                // far inside that cache's tolerance, so no tail
+                for (int j = 0; j < 4; ++j) {
+                    h[j] = pack_bf16(p[2 * j], p[2 * j + 1]);
+                    lsum += bf16_lo(h[j]) + bf16_hi(h[j]);
+                }
+                const u32x4 ph = u32x4{h[0], h[1], h[2], h[3]};
 #pragma unroll
                 for (int dt = 0; dt < D / 32; ++dt) {
                     const u32x4 vb =
@@ -435,6 +439,13 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
                     o[dt] = mfma32(ph, vb, o[dt]);
                 }
             } else {
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    lsum += p[j];
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    h[j] = pack_bf16(p[2 * j], p[2 * j + 1]);
+                const u32x4 ph = u32x4{h[0], h[1], h[2], h[3]};
                 uint32_t t[4];
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
@@ -451,12 +462,14 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
         });
     };
 
-    auto compute_tile = [&](const char *kt_lds, const char *vt_lds, int kt) {
+    auto compute_tile = [&](const char *kt_lds, const char *vt_lds, int kt, auto mode) {
         f32x16 s[2];
         s_tile(kt_lds, s);
         const float mu = mask_max(s, kt);
-        pv_tile(s, mu, vt_lds);
+        pv_tile(s, mu, vt_lds, mode);
     };
+    using Mode0 = std::integral_constant<int, 0>;
+    using Mode1 = std::integral_constant<int, 1>;
     if constexpr (!C::RAW) {
         // the ring stages are the compute tiles
         for (int u = 0; u < NS - 1 && u < nt; ++u)
@@ -469,7 +482,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
             if (u + NS - 1 < nt)
                 issue_tile(kt + NS - 1, (u + NS - 1) % NS);
             const char *st_lds = sm.ring + (u % NS) * C::STAGEB;
-            compute_tile(st_lds, st_lds + C::TILEB, kt);
+            compute_tile(st_lds, st_lds + C::TILEB, kt, Mode0{});
         }
     } else {
         // raw ring -> widened double buffer, one tile ahead of the compute
@@ -490,7 +503,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
             if (u + NS - 1 < nt)
                 issue_tile(kt + NS - 1, (u + NS - 1) % NS);
             const char *cb_lds = sm.ring + NS * C::STAGEB + (u & 1) * 2 * C::TILEB;
-            compute_tile(cb_lds, cb_lds + C::TILEB, kt);
+            compute_tile(cb_lds, cb_lds + C::TILEB, kt, Mode1{});
             if (u + 1 < nt)
                 widen_tile((u + 1) % NS, (u + 1) & 1);
         }

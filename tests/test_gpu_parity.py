@@ -440,6 +440,27 @@ def test_prefill_cases(storage, hc):
     assert max_err(out.cpu().numpy(), ref) <= TOL[storage]
 
 
+@pytest.mark.parametrize("big", [7e4, 1e30])
+def test_prefill_v_beyond_fp16_range(big):
+    """A bf16 cache whose V rows reach magnitudes fp16 cannot hold: the P V
+    products take bf16 operands throughout, so they come out finite."""
+    p, qp, qs = _prefill_problem(17, [(600, 150)], 16, 4, 128, "bf16")
+    vflat = p["v"].view(-1, 4, 128)
+    slots = [int(p["bt_h"][0, 3]) * 16 + 5, int(p["bt_h"][0, 30]) * 16 + 2]
+    for s_ in slots:
+        vflat[s_, 1, :8] = big  # two keys (tiles 0 and 7) of KV head 1
+    p["v_h"] = host_bits(p["v"])
+    out = torch.full(qp.shape, float("nan"), dtype=torch.float32, device="cuda")
+    binding.prefill_chunk(out, qp, p["k"], p["v"], p["bt"], to_dev(qs), p["lens"], p["scale"])
+    torch.cuda.synchronize()
+    ref = oracle.prefill(host_bits(qp), pool_rows(p["k_h"]), pool_rows(p["v_h"]), p["bt_h"], qs,
+                         p["lens_h"], p["scale"])
+    got = out.cpu().numpy()
+    assert np.all(np.isfinite(got))
+    # fp32 accumulation of values near `big`: compare relative to the magnitude
+    assert np.max(np.abs(got - ref) / (1.0 + np.abs(ref))) <= 2e-3
+
+
 def test_prefill_one_row_matches_decode():
     p, qp, qs = _prefill_problem(12, [(500, 1)], 28, 4, 128, "bf16")
     out = torch.empty(qp.shape, dtype=torch.float32, device="cuda")
