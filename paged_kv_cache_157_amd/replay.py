@@ -2,7 +2,9 @@
 step over a stream of synthetic requests.
 
 Each step: the scheduler plans (decodes first, then prefill chunks under the
-token budget); any copy-on-write copies run (pa_copy_blocks); the step's new
+token budget); blocks of requests preempted in this step go to pinned host
+pools and blocks of resumed ones come back (pa_swap_blocks); any
+copy-on-write copies run (pa_copy_blocks); the step's new
 K/V rows go into the cache (pa_reshape_and_cache); the chunks attend their
 paged history (pa_prefill_chunk) and the decodes theirs (pa_decode); finished
 requests return their blocks.  Request lengths, q rows and new K/V rows are
@@ -12,7 +14,7 @@ the projections of a model.
 Sources, cited by page title and section: "Lecture 33: KV Cache memory
 management -- PagedAttention, Continuous Batching and Chunked Prefill" §3.2
 (iteration-level scheduling), §4.2-4.4 (chunked prefill under one token
-budget); "PagedAttention: managing the KV cache like virtual memory" §3.3
+budget), §5.2 (preemption by swapping); "PagedAttention: managing the KV cache like virtual memory" §3.3
 (blocks taken as sequences grow, returned as they end).
 """
 from __future__ import annotations
@@ -46,6 +48,8 @@ class ReplayConfig:
     output: Tuple[int, int]   # uniform output lengths, closed range
     seed: int
     kv_scale: float = 1.0
+    decode_reserve: bool = True  # False: admit greedily, preempt by swapping
+    host_blocks: int = 0         # blocks of the pinned host pools (swap space)
 
     @property
     def scale(self) -> float:
@@ -86,7 +90,9 @@ class Replay:
         self.dev = device
         self.keep = keep
         self.pool = BlockPool(cfg.num_blocks, seed=cfg.seed)
-        self.sched = Scheduler(self.pool, cfg.budget)
+        self.host_pool = BlockPool(cfg.host_blocks, seed=cfg.seed + 1) if cfg.host_blocks else None
+        self.sched = Scheduler(self.pool, cfg.budget, decode_reserve=cfg.decode_reserve,
+                               host_pool=self.host_pool)
         for r in synthetic_requests(cfg.num_requests, cfg.seed, cfg.prompt, cfg.output):
             self.sched.add(r)
         g = torch.Generator(device=device)
@@ -96,6 +102,11 @@ class Replay:
         # recycled blocks hold stale rows, never zeros: start from random bits
         self.k_cache = torch.randn(shape, generator=g, device=device).to(cdt)
         self.v_cache = torch.randn(shape, generator=g, device=device).to(cdt)
+        self.k_host = self.v_host = None
+        if cfg.host_blocks:
+            hshape = (cfg.host_blocks,) + shape[1:]
+            self.k_host = torch.empty(hshape, dtype=cdt).pin_memory()
+            self.v_host = torch.empty(hshape, dtype=cdt).pin_memory()
         # step rows are slices of fixed random buffers (budget rows each)
         B = cfg.budget
         self.q_buf = torch.randn((B, cfg.num_q_heads, cfg.head_dim), generator=g,
@@ -131,10 +142,16 @@ class Replay:
             bt, lens = plan.decode_inputs(cfg.width)
             dec = dict(bt=to_dev(bt), lens=to_dev(lens), host=(bt, lens))
         cow = to_dev(np.asarray(plan.cow, dtype=np.int64).reshape(-1, 2)) if plan.cow else None
+        pairs = lambda x: to_dev(np.asarray(x, dtype=np.int64).reshape(-1, 2)) if x else None
+        s_out, s_in = pairs(plan.swap_out), pairs(plan.swap_in)
         q = self.q_buf[:T]
         out = self.out_buf[:T]
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
+        if s_out is not None:  # before anything reuses the freed device blocks
+            binding.swap_blocks(self.k_cache, self.v_cache, self.k_host, self.v_host, s_out)
+        if s_in is not None:
+            binding.swap_blocks(self.k_host, self.v_host, self.k_cache, self.v_cache, s_in)
         if cow is not None:
             binding.copy_blocks(self.k_cache, self.v_cache, cow)
         binding.reshape_and_cache(self.k_buf[:T], self.v_buf[:T], self.k_cache, self.v_cache, sm,
@@ -174,6 +191,7 @@ def run(cfg: ReplayConfig, device: torch.device, max_steps: Optional[int] = None
     toks = sum(r.plan.num_tokens for r in ss)
     kv = sum(r.decode_ctx_tokens for r in ss) * cfg.kv_bytes_per_token
     return dict(steps=len(recs), steady_steps=len(ss), finished=len(rp.sched.finished),
+                preemptions=rp.sched.preemptions,
                 wall_s=round(wall, 2),
                 gpu_ms_per_step=round(gpu_s * 1e3 / len(ss), 4),
                 tokens_per_s_gpu=round(toks / gpu_s, 1),

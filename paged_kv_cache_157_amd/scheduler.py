@@ -20,13 +20,21 @@ Sources, cited by page title and section:
         through the cache), §4.3 (one token budget for prefill and decode
         alike), §4.4 (decodes first, one token each; the rest of the budget
         cut into prefill chunks).
+        §5.1-5.2 (when a decode finds no free block, the youngest running
+        request is preempted: its blocks go to host memory over PCIe and come
+        back when there is room).
   [VM]  "PagedAttention: managing the KV cache like virtual memory": §3.3
         (blocks are taken as a sequence grows and returned when it ends).
 
-Preemption (swap or recompute) is out of scope: a decode that finds no free
-block raises PoolExhausted.  A prefill chunk is admitted only while one free
-block per running decode remains after it (so the decodes can grow);
-otherwise it waits, with every later prompt, for a later step.
+Two admission policies: with ``decode_reserve`` (the default) a prefill chunk
+is admitted only while one free block per running decode remains after it,
+so the decodes can always grow and nothing is preempted; without it chunks
+are admitted while blocks are free, and a decode that then finds none
+preempts running requests youngest first, swapping their blocks to the host
+pool (recomputation is out of scope: it needs a model).  Swapped requests
+resume in the order they were preempted, at the start of a step, once their
+blocks fit.  Without a host pool a decode that finds no block raises
+PoolExhausted.
 """
 from __future__ import annotations
 
@@ -36,7 +44,7 @@ from typing import Deque, List, Optional, Tuple
 
 import numpy as np
 
-from .block_manager import BLOCK_SIZE, BlockPool, SeqTable
+from .block_manager import BLOCK_SIZE, BlockPool, PoolExhausted, SeqTable, swap_in, swap_out
 
 
 @dataclass
@@ -51,6 +59,7 @@ class Request:
     generated: int = 0    # output tokens produced so far
     first_step: int = -1  # step of the first chunk
     done_step: int = -1   # step that produced the last output token
+    preempted: int = 0    # times swapped out
 
     @property
     def decoding(self) -> bool:
@@ -73,6 +82,11 @@ class StepPlan:
     decode_slots: List[int]
     chunks: List[Chunk]
     cow: List[Tuple[int, int]] = field(default_factory=list)
+    # block moves to run before anything else in the step: device -> host
+    # (preempted requests), then host -> device (resumed ones)
+    swap_out: List[Tuple[int, int]] = field(default_factory=list)
+    swap_in: List[Tuple[int, int]] = field(default_factory=list)
+    preempted: List[Request] = field(default_factory=list)
 
     @property
     def num_tokens(self) -> int:
@@ -111,16 +125,21 @@ class StepPlan:
 class Scheduler:
     """Admits, grows and retires requests under a per-step token budget."""
 
-    def __init__(self, pool: BlockPool, budget: int = 2048, max_chunk: Optional[int] = None):
+    def __init__(self, pool: BlockPool, budget: int = 2048, max_chunk: Optional[int] = None,
+                 decode_reserve: bool = True, host_pool: Optional[BlockPool] = None):
         if budget <= 0:
             raise ValueError("budget must be positive")
         self.pool = pool
         self.budget = int(budget)
         self.max_chunk = max_chunk
+        self.decode_reserve = decode_reserve
+        self.host = host_pool
         self.waiting: Deque[Request] = deque()   # arrival order, prefill not finished
-        self.running: List[Request] = []         # decoding
+        self.running: List[Request] = []         # decoding, oldest first
+        self.swapped: Deque[Request] = deque()   # preempted, in preemption order
         self.finished: List[Request] = []
         self.step_no = 0
+        self.preemptions = 0
 
     def add(self, req: Request) -> None:
         if req.prompt_len <= 0 or req.output_len <= 0:
@@ -129,23 +148,48 @@ class Scheduler:
 
     @property
     def idle(self) -> bool:
-        return not self.waiting and not self.running
+        return not self.waiting and not self.running and not self.swapped
 
     def schedule(self) -> StepPlan:
         """Plan one step ([L33] §4.4)."""
         left = self.budget
         plan = StepPlan(self.step_no, [], [], [])
-        # phase 1: every running decode gets one token (its newest token's KV
-        # is written and it attends everything up to it)
-        for r in self.running:
-            if left == 0:
+        # phase 0: preempted requests come back, in preemption order, while
+        # their blocks fit next to one free block per running decode
+        while self.swapped:
+            r = self.swapped[0]
+            if len(r.table.blocks) + len(self.running) + 1 > self.pool.num_free:
                 break
+            plan.swap_in += swap_in(r.table, self.pool)
+            self.swapped.popleft()
+            self.running.append(r)
+        # phase 1: every running decode gets one token (its newest token's KV
+        # is written and it attends everything up to it), oldest first; one
+        # that finds no free block preempts the youngest until one is free
+        i = 0
+        while i < len(self.running) and left > 0:
+            r = self.running[i]
+            needs_block = r.table.num_tokens == len(r.table.blocks) * BLOCK_SIZE
+            while needs_block and self.pool.num_free == 0:
+                if self.host is None:
+                    raise PoolExhausted("a decode needs a block and nothing can be preempted")
+                victim = self.running.pop()  # the youngest
+                plan.swap_out += swap_out(victim.table, self.host)
+                victim.preempted += 1
+                self.preemptions += 1
+                self.swapped.append(victim)
+                plan.preempted.append(victim)
+                if victim is r:
+                    break
+            if r not in self.running:
+                break  # r preempted itself: every older one is served
             slot, cow = r.table.append_token()
             if cow is not None:
                 plan.cow.append(cow)
             plan.decodes.append(r)
             plan.decode_slots.append(slot)
             left -= 1
+            i += 1
         # phase 2: prefill chunks in arrival order from what is left
         for r in self.waiting:
             if left == 0:
@@ -158,16 +202,20 @@ class Scheduler:
                 r.table = SeqTable(self.pool)
             have = len(r.table.blocks) * BLOCK_SIZE - r.table.num_tokens
             new_blocks = -(-max(0, n - have) // BLOCK_SIZE)
-            # keep one free block per running decode, so that every decode
-            # can still grow by a block in the next step
-            if new_blocks > self.pool.num_free - len(self.running):
-                break  # no room: this prompt and every later one wait
+            # with the reserve: keep one free block per running decode, so that
+            # every decode can still grow by a block in the next step
+            reserve = len(self.running) if self.decode_reserve else 0
+            if (self.swapped and r.prefilled == 0) or new_blocks > self.pool.num_free - reserve:
+                break  # no room, or preempted requests go first: this prompt and later ones wait
             slots, cows = r.table.extend(n)
             plan.cow += cows
             if r.first_step < 0:
                 r.first_step = self.step_no
             plan.chunks.append(Chunk(r, r.prefilled, n, slots))
             left -= n
+        if plan.num_tokens == 0 and not self.idle:
+            raise PoolExhausted("no request can make progress: the pool is held by waiting prompts "
+                                "and preempted requests")
         return plan
 
     def complete(self, plan: StepPlan) -> List[Request]:

@@ -21,6 +21,11 @@ SMALL = [
     # head groups (Hkv = 8, G = 4), fp8
     ReplayConfig("r_fp8", 32, 8, 128, "fp8", num_blocks=230, budget=256, num_requests=24,
                  prompt=(1, 300), output=(1, 40), seed=72, kv_scale=0.05),
+    # greedy admission into a small pool: decodes that find no block preempt
+    # the youngest requests, whose blocks go to host memory and come back
+    ReplayConfig("r_swap", 16, 4, 128, "bf16", num_blocks=160, budget=256, num_requests=40,
+                 prompt=(16, 400), output=(20, 200), seed=6, decode_reserve=False,
+                 host_blocks=400),
 ]
 
 
@@ -31,7 +36,8 @@ def test_replay_steps_match_the_oracle(cfg):
     while not rp.done:
         rec = rp.step()
         st = rp.last
-        if rec.plan.step % 3:
+        every = 3 if cfg.decode_reserve else 12  # and every step that moved blocks
+        if rec.plan.step % every and not (rec.plan.swap_in or rec.plan.swap_out):
             continue
         say(f"replay {cfg.name} step {rec.plan.step}: {st['n_pre']} prefill rows, {st['D']} decodes")
         kp = pool_rows(host_bits(rp.k_cache))
@@ -51,4 +57,6 @@ def test_replay_steps_match_the_oracle(cfg):
         mixed += st["pre"] is not None and st["dec"] is not None
     assert len(rp.sched.finished) == cfg.num_requests
     assert checked >= 10 and mixed >= 3
+    if not cfg.decode_reserve:
+        assert rp.sched.preemptions > 0
     assert rp.pool.num_free == cfg.num_blocks  # every block returned

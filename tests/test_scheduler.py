@@ -133,3 +133,64 @@ def test_seeded_replay_invariants():
         assert seen_decode[r.rid] == r.output_len - 1
         assert r.generated == r.output_len and r.done_step >= r.first_step
     assert pool.num_free == 3000 and not pool.ref_counts().any()
+
+
+# ----------------------------------------------------------------------------
+# preemption by swapping ([L33] §5.1-5.2)
+# ----------------------------------------------------------------------------
+
+def test_decode_without_a_block_preempts_the_youngest():
+    pool, host = BlockPool(6), BlockPool(20)
+    s = Scheduler(pool, budget=64, decode_reserve=False, host_pool=host)
+    a, b = Request(0, 32, 30), Request(1, 32, 30)
+    s.add(a)
+    s.add(b)
+    s.complete(s.schedule())  # step 0: both prompts (2 blocks each); first output tokens
+    assert s.running == [a, b] and pool.num_free == 2
+    s.complete(s.schedule())  # step 1: position 32 of each takes a new block
+    assert pool.num_free == 0
+    for _ in range(15):       # steps 2-16: positions 33-47 fill those blocks
+        s.complete(s.schedule())
+    p = s.schedule()          # step 17: a needs a 4th block, b (the youngest) goes out
+    assert p.preempted == [b] and p.decodes == [a]
+    assert len(p.swap_out) == 3 and b.table.pool is host and list(s.swapped) == [b]
+    assert s.preemptions == 1 and pool.num_free == 2
+    s.complete(p)
+    resumed = None
+    while b in s.swapped:     # b returns once a has finished and freed its blocks
+        p = s.schedule()
+        if p.swap_in:
+            resumed = p
+        s.complete(p)
+    assert a.done_step == 29 and resumed.step == 30 and len(resumed.swap_in) == 3
+    assert resumed.decodes == [b] and b.table.pool is pool
+    run_until_idle(s)
+    assert a.generated == b.generated == 30 and b.preempted == 1
+    assert pool.num_free == 6 and host.num_free == 20
+
+
+def test_seeded_replay_with_preemption_invariants():
+    pool, host = BlockPool(160, seed=2), BlockPool(400, seed=3)
+    budget = 256
+    s = Scheduler(pool, budget=budget, decode_reserve=False, host_pool=host)
+    reqs = synthetic_requests(40, seed=6, prompt=(16, 400), output=(20, 200))
+    for r in reqs:
+        s.add(r)
+    decoded = {r.rid: 0 for r in reqs}
+    while not s.idle:
+        running_before = list(s.running)
+        p = s.schedule()
+        assert p.num_tokens <= budget
+        for v in p.preempted:  # victims are the youngest running requests
+            assert v is running_before[len(running_before) - 1 - p.preempted.index(v)]
+        moved_out = [d for d, _ in p.swap_out]
+        assert len(set(moved_out)) == len(moved_out)
+        for r in p.decodes:
+            decoded[r.rid] += 1
+            assert r.table.pool is pool
+        s.complete(p)
+    assert s.preemptions > 0
+    for r in reqs:
+        assert r.generated == r.output_len and decoded[r.rid] == r.output_len - 1
+    assert pool.num_free == 160 and host.num_free == 400
+    assert not pool.ref_counts().any() and not host.ref_counts().any()
