@@ -323,6 +323,34 @@ def main():
                             swap_time_model(n * 16, kv_bytes_per_token(cfg), link) * 1e6, 1))
         del hk, hv, flat_d, flat_h
 
+    # block-size trade-off ([L33] §2.2, appendix Q3): the batch's lengths
+    # decoded from pools of 16-, 32- and 64-token blocks, scattered at random
+    bs_res = None
+    if args.extras and cfg.cache_dtype == "bf16":
+        bs_res = {}
+        L = step.plan.context_lens.astype(np.int64)
+        for B in (16, 32, 64):
+            nbs = (L + B - 1) // B
+            nblk = int(nbs.sum()) + 64
+            rng = np.random.default_rng(cfg.seed + B)
+            perm = rng.permutation(nblk)
+            bt = np.full((len(L), int(nbs.max())), -1, np.int32)
+            c = 0
+            for i, n in enumerate(nbs):
+                bt[i, :n] = perm[c:c + n]
+                c += n
+            shp = (nblk, B, cfg.num_kv_heads, cfg.head_dim)
+            kb = torch.randn(shp, device=dev).to(torch.bfloat16)
+            vb = torch.randn(shp, device=dev).to(torch.bfloat16)
+            bt_d = torch.from_numpy(bt).to(dev)
+            run = lambda: binding.decode(out, step.q, kb, vb, bt_d, step.context_lens, cfg.scale)
+            for _ in range(50):
+                run()
+            us = launch_ms(run, 300) * 1e3
+            bs_res[str(B)] = dict(decode_us=round(us, 2), table_entries=int(nbs.sum()),
+                                  tail_waste_tokens=int((nbs * B - L).sum()))
+            del kb, vb
+
     dec_cold = copy_gbs = None
     if args.extras:
         evict = torch.ones(192 << 20, dtype=torch.float32, device=dev)  # 768 MiB
@@ -393,6 +421,7 @@ def main():
         "cache_write_us": round(cw_ms * 1e3, 2),
         "copy_blocks": copy_res,
         "swap_blocks": swap_res,
+        "block_size_sweep": bs_res,
         "decode_kv_gbs": round(ab["kv"] / (dec_ms * 1e-3) / 1e9, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),

@@ -68,7 +68,7 @@ typedef struct {
     int32_t num_q_heads;        /* Hq                                                */
     int32_t num_kv_heads;       /* Hkv; Hq % Hkv == 0 and Hq / Hkv <= 8              */
     int32_t head_dim;           /* d: 64 or 128 (f32 cache: 64 only)                 */
-    int64_t num_blocks;         /* N physical blocks of 16 token slots               */
+    int64_t num_blocks;         /* N physical blocks of block_size token slots       */
     int32_t max_blocks_per_seq; /* width of block_tables                             */
     int32_t q_dtype;            /* pa_dtype of q: PA_F32 with an f32 cache, else BF16 */
     int32_t cache_dtype;        /* pa_dtype of the pools                             */
@@ -76,6 +76,10 @@ typedef struct {
     int32_t partition_tokens;   /* decode split-K: 0 = balanced split over the whole
                                    GPU, else fixed partitions of this many tokens
                                    (a multiple of 16)                               */
+    int32_t block_size;         /* tokens per block: 16 (0 also means 16), 32 or 64;
+                                   [L33] §2.2: token t of a sequence lives in slot
+                                   table[t / block_size] * block_size
+                                   + t % block_size                                  */
 } pa_shape;
 
 /*

@@ -56,11 +56,11 @@ def _load():
         lib.oracle_swap_blocks.restype = None
         lib.oracle_decode.argtypes = [P, P, ctypes.c_int, P, P, ctypes.c_int, dbl, P, i32, P,
                                       ctypes.c_int, ctypes.c_int, ctypes.c_int, dbl, P, P, i64,
-                                      ctypes.c_int]
+                                      ctypes.c_int, ctypes.c_int]
         lib.oracle_decode.restype = ctypes.c_int
         lib.oracle_prefill.argtypes = [P, P, ctypes.c_int, P, P, ctypes.c_int, dbl, P, i32, P, P,
                                        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, dbl,
-                                       P, P, i64, ctypes.c_int]
+                                       P, P, i64, ctypes.c_int, ctypes.c_int]
         lib.oracle_prefill.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -109,33 +109,34 @@ def reshape_and_cache(k, v, k_cache, v_cache, slot_mapping, kv_scale: float = 1.
                                      _dtype_code(k_cache), hkv, d, float(kv_scale))
 
 
-def copy_blocks(k_cache, v_cache, pairs) -> None:
-    """Copy-on-write of whole blocks in host pools ([slots, Hkv, d], 16 slots
-    per block), in place: for each (src, dst) row of ``pairs``, in order,
-    block dst of both pools becomes a copy of block src."""
+def copy_blocks(k_cache, v_cache, pairs, block_size: int = 16) -> None:
+    """Copy-on-write of whole blocks in host pools ([slots, Hkv, d],
+    block_size slots per block), in place: for each (src, dst) row of
+    ``pairs``, in order, block dst of both pools becomes a copy of block src."""
     pairs = np.ascontiguousarray(np.asarray(pairs, dtype=np.int64).reshape(-1, 2))
     assert v_cache.shape == k_cache.shape and v_cache.dtype == k_cache.dtype
-    assert k_cache.shape[0] % 16 == 0
-    block_bytes = 16 * k_cache.shape[1] * k_cache.shape[2] * k_cache.itemsize
+    assert k_cache.shape[0] % block_size == 0
+    block_bytes = block_size * k_cache.shape[1] * k_cache.shape[2] * k_cache.itemsize
     _load().oracle_copy_blocks(_ptr(k_cache), _ptr(v_cache), _ptr(pairs), pairs.shape[0],
-                               k_cache.shape[0] // 16, block_bytes)
+                               k_cache.shape[0] // block_size, block_bytes)
 
 
-def swap_blocks(src_k, src_v, dst_k, dst_v, pairs) -> None:
-    """Block moves between two host pool pairs ([slots, Hkv, d], 16 slots per
-    block): for each (src, dst) row of ``pairs``, in order, block dst of the
-    destination pools becomes a copy of block src of the source pools."""
+def swap_blocks(src_k, src_v, dst_k, dst_v, pairs, block_size: int = 16) -> None:
+    """Block moves between two host pool pairs ([slots, Hkv, d], block_size
+    slots per block): for each (src, dst) row of ``pairs``, in order, block
+    dst of the destination pools becomes a copy of block src of the source
+    pools."""
     pairs = np.ascontiguousarray(np.asarray(pairs, dtype=np.int64).reshape(-1, 2))
     assert src_k.shape[1:] == dst_k.shape[1:] and src_k.dtype == dst_k.dtype
     assert src_v.shape == src_k.shape and dst_v.shape == dst_k.shape
-    block_bytes = 16 * src_k.shape[1] * src_k.shape[2] * src_k.itemsize
-    _load().oracle_swap_blocks(_ptr(src_k), _ptr(src_v), src_k.shape[0] // 16, _ptr(dst_k),
-                               _ptr(dst_v), dst_k.shape[0] // 16, _ptr(pairs), pairs.shape[0],
+    block_bytes = block_size * src_k.shape[1] * src_k.shape[2] * src_k.itemsize
+    _load().oracle_swap_blocks(_ptr(src_k), _ptr(src_v), src_k.shape[0] // block_size, _ptr(dst_k),
+                               _ptr(dst_v), dst_k.shape[0] // block_size, _ptr(pairs), pairs.shape[0],
                                block_bytes)
 
 
 def decode(q, k_cache, v_cache, block_tables, context_lens, scale, kv_scale=1.0,
-           sel_seq=None, sel_head=None, num_threads=None):
+           sel_seq=None, sel_head=None, num_threads=None, block_size: int = 16):
     """Decode attention for (seq, head) pairs; returns float64 [n_sel, d].
 
     q: [S, Hq, d] float32 or uint16 (bf16 bits); pools: [slots, Hkv, d].
@@ -157,14 +158,14 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, scale, kv_scale=1.0,
                                _dtype_code(k_cache), float(kv_scale), _ptr(block_tables),
                                block_tables.shape[1], _ptr(context_lens), hq, hkv, d,
                                float(scale), _ptr(sel_seq), _ptr(sel_head), len(sel_seq),
-                               num_threads or default_threads())
+                               num_threads or default_threads(), int(block_size))
     if rc != 0:
         raise ValueError(f"oracle_decode failed ({rc})")
     return out.reshape(S, hq, d) if full else out
 
 
 def prefill(q, k_cache, v_cache, block_tables, query_start, context_lens, scale, kv_scale=1.0,
-            sel_row=None, sel_head=None, num_threads=None):
+            sel_row=None, sel_head=None, num_threads=None, block_size: int = 16):
     """Chunked-prefill attention for (row, head) pairs; returns float64 [n_sel, d]."""
     Tq, hq, d = q.shape
     hkv = k_cache.shape[1]
@@ -183,7 +184,8 @@ def prefill(q, k_cache, v_cache, block_tables, query_start, context_lens, scale,
                                 _dtype_code(k_cache), float(kv_scale), _ptr(block_tables),
                                 block_tables.shape[1], _ptr(query_start), _ptr(context_lens),
                                 len(context_lens), hq, hkv, d, float(scale), _ptr(sel_row),
-                                _ptr(sel_head), len(sel_row), num_threads or default_threads())
+                                _ptr(sel_head), len(sel_row), num_threads or default_threads(),
+                                int(block_size))
     if rc != 0:
         raise ValueError(f"oracle_prefill failed ({rc})")
     return out.reshape(Tq, hq, d) if full else out

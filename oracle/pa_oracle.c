@@ -171,10 +171,10 @@ void oracle_reshape_and_cache(const void *k, const void *v, void *k_cache, void 
     }
 }
 
-/* Copy-on-write ([L33] §2.4): for every (src, dst) pair, in order, the 16
+/* Copy-on-write ([L33] §2.4): for every (src, dst) pair, in order, the
  * token rows of block src in both pools are copied over the rows of block
- * dst (pools [num_slots, Hkv, d], block b = slots 16b .. 16b + 15).  A pair
- * naming a block outside [0, num_blocks) is skipped. */
+ * dst (pools [num_slots, Hkv, d]; a block is block_bytes of consecutive
+ * rows).  A pair naming a block outside [0, num_blocks) is skipped. */
 void oracle_copy_blocks(void *k_cache, void *v_cache, const int64_t *pairs, int64_t num_pairs,
                         int64_t num_blocks, int64_t block_bytes)
 {
@@ -221,6 +221,7 @@ typedef struct {
     double kv_scale;
     const int32_t *block_tables;
     int32_t max_blocks_per_seq;
+    int32_t block_size;        /* tokens per block */
     int num_q_heads, num_kv_heads, head_dim;
     double scale;
     /* decode: query row of seq i is row i; prefill: row index given */
@@ -235,15 +236,17 @@ typedef struct {
     pthread_mutex_t lock;
 } attn_job;
 
-/* Physical slot of logical token t of sequence `seq`:
- * logical block t / 16, offset t % 16, physical block from the table
- * ([L33] §2.2 walk-through; the same formula in its appendix Q1). */
+/* Physical slot of logical token t of sequence `seq`: logical block
+ * t / B, offset t % B, physical block from the table, slot = block * B +
+ * offset, for B tokens per block ([L33] §2.2 walk-through with B = 16; the
+ * same formula in its appendix Q1). */
 static int64_t token_slot(const attn_job *J, int seq, int64_t t)
 {
-    int64_t logical_block = t / 16;
-    int64_t offset = t % 16;
+    int64_t B = J->block_size;
+    int64_t logical_block = t / B;
+    int64_t offset = t % B;
     int64_t physical_block = J->block_tables[(int64_t)seq * J->max_blocks_per_seq + logical_block];
-    return physical_block * 16 + offset;
+    return physical_block * B + offset;
 }
 
 /* One output row: softmax(scale * q K^T) V over keys [0, nkeys). */
@@ -335,11 +338,11 @@ int oracle_decode(double *out, const void *q, int q_dtype, const void *k_cache,
                   const int32_t *block_tables, int32_t max_blocks_per_seq,
                   const int32_t *context_lens, int num_q_heads, int num_kv_heads,
                   int head_dim, double scale, const int32_t *sel_seq,
-                  const int32_t *sel_head, int64_t num_sel, int num_threads)
+                  const int32_t *sel_head, int64_t num_sel, int num_threads, int block_size)
 {
     attn_job J;
     int32_t *nkeys;
-    if (num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0)
+    if (num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0 || block_size <= 0)
         return -1;
     nkeys = (int32_t *)malloc((size_t)(num_sel > 0 ? num_sel : 1) * sizeof(int32_t));
     if (!nkeys)
@@ -351,6 +354,7 @@ int oracle_decode(double *out, const void *q, int q_dtype, const void *k_cache,
     J.k_cache = k_cache; J.v_cache = v_cache; J.cache_dtype = cache_dtype;
     J.kv_scale = kv_scale;
     J.block_tables = block_tables; J.max_blocks_per_seq = max_blocks_per_seq;
+    J.block_size = block_size;
     J.num_q_heads = num_q_heads; J.num_kv_heads = num_kv_heads; J.head_dim = head_dim;
     J.scale = scale;
     J.item_row = sel_seq; J.item_seq = sel_seq; J.item_head = sel_head;
@@ -372,11 +376,11 @@ int oracle_prefill(double *out, const void *q, int q_dtype, const void *k_cache,
                    const int32_t *query_start, const int32_t *context_lens,
                    int num_requests, int num_q_heads, int num_kv_heads, int head_dim,
                    double scale, const int32_t *sel_row, const int32_t *sel_head,
-                   int64_t num_sel, int num_threads)
+                   int64_t num_sel, int num_threads, int block_size)
 {
     attn_job J;
     int32_t *nkeys, *seq;
-    if (num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0)
+    if (num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0 || block_size <= 0)
         return -1;
     nkeys = (int32_t *)malloc((size_t)(num_sel > 0 ? num_sel : 1) * sizeof(int32_t));
     seq = (int32_t *)malloc((size_t)(num_sel > 0 ? num_sel : 1) * sizeof(int32_t));
@@ -407,6 +411,7 @@ int oracle_prefill(double *out, const void *q, int q_dtype, const void *k_cache,
     J.k_cache = k_cache; J.v_cache = v_cache; J.cache_dtype = cache_dtype;
     J.kv_scale = kv_scale;
     J.block_tables = block_tables; J.max_blocks_per_seq = max_blocks_per_seq;
+    J.block_size = block_size;
     J.num_q_heads = num_q_heads; J.num_kv_heads = num_kv_heads; J.head_dim = head_dim;
     J.scale = scale;
     J.item_row = sel_row; J.item_seq = seq; J.item_head = sel_head;

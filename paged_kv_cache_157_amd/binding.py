@@ -35,6 +35,7 @@ class PAShape(ctypes.Structure):
         ("cache_dtype", ctypes.c_int32),
         ("kv_scale", ctypes.c_float),
         ("partition_tokens", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
     ]
 
 
@@ -107,15 +108,16 @@ def _require(t: torch.Tensor, name: str, device: torch.device, dtype=None, ndim=
 
 def make_shape(q_heads: int, k_cache: torch.Tensor, q_dtype: torch.dtype, num_seqs: int,
                max_blocks: int, kv_scale: float = 1.0, partition_tokens: int = 0) -> PAShape:
-    if k_cache.dim() != 4 or k_cache.shape[1] != 16:
-        raise ValueError("KV pools must be [num_blocks, 16, num_kv_heads, head_dim]")
+    if k_cache.dim() != 4 or k_cache.shape[1] not in (16, 32, 64):
+        raise ValueError("KV pools must be [num_blocks, block_size, num_kv_heads, head_dim] "
+                         "with block_size 16, 32 or 64")
     if k_cache.dtype not in _DTYPES or q_dtype not in _DTYPES:
         raise ValueError(f"unsupported dtypes {q_dtype} / {k_cache.dtype}")
     return PAShape(num_seqs=num_seqs, num_q_heads=q_heads, num_kv_heads=k_cache.shape[2],
                    head_dim=k_cache.shape[3], num_blocks=k_cache.shape[0],
                    max_blocks_per_seq=max_blocks, q_dtype=_DTYPES[q_dtype],
                    cache_dtype=_DTYPES[k_cache.dtype], kv_scale=float(kv_scale),
-                   partition_tokens=int(partition_tokens))
+                   partition_tokens=int(partition_tokens), block_size=k_cache.shape[1])
 
 
 _workspaces: Dict[Tuple[int, str], torch.Tensor] = {}

@@ -236,11 +236,17 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(DecodeArgs a)
     const int w = uniform(tid >> 6);
     const int S = a.num_seqs, Hkv = a.num_kv_heads, Hq = a.num_q_heads, maxB = a.max_blocks;
     const int PB = a.part_blocks;
+    // the kernel walks 16-token units; a table entry names 2^ts consecutive ones
+    const int ts = a.tbs_log2;
+    const int maxU = maxB << ts;  // units a table row addresses
+    auto unit_block = [&](auto tab, int u) -> int {
+        return (tab[u >> ts] << ts) + (u & ((1 << ts) - 1));
+    };
 
     auto items_of = [&](int L) -> int {
         L = L < 0 ? 0 : L;
         int nb = (L + 15) >> 4;
-        nb = nb > maxB ? maxB : nb;
+        nb = nb > maxU ? maxU : nb;
         return PB > 0 ? (nb + PB - 1) / PB : nb;
     };
 
@@ -254,9 +260,9 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(DecodeArgs a)
     constexpr int ALPHA = DECODE_SEGCOST;
     if (w == 0) {
         const long long W = gridDim.x;
-        // 64 lanes' item counts fit 32 bits whenever (maxB + ALPHA) * Hkv * 64
+        // 64 lanes' item counts fit 32 bits whenever (maxU + ALPHA) * Hkv * 64
         // does: DPP scans then; otherwise shuffles on 64-bit values
-        const bool narrow = (long long)(maxB + ALPHA) * Hkv * 64 < (1ll << 31);
+        const bool narrow = (long long)(maxU + ALPHA) * Hkv * 64 < (1ll << 31);
         auto scan = [&](long long v) -> long long {
             if (narrow)
                 return wave_scan32((int)v);
@@ -441,7 +447,7 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(DecodeArgs a)
             L = lens_s[si];
             n = items_of(L);
         }
-        d.L = uniform(L > maxB * 16 ? maxB * 16 : L);
+        d.L = uniform(L > maxU * 16 ? maxU * 16 : L);
         d.n_i = uniform(n);
         const long long rel = it - sbase;
         d.g = uniform((int)(rel / d.n_i));
@@ -483,7 +489,7 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(DecodeArgs a)
     auto issue_first = [&](int si, const Seg &d) -> bool {
         if (d.b0 + w >= d.b1)
             return false;
-        const int pb0 = uniform(scalar_view(a.block_tables + (int64_t)si * maxB)[d.b0 + w]);
+        const int pb0 = uniform(unit_block(scalar_view(a.block_tables + (int64_t)si * maxB), d.b0 + w));
         const unsigned pb = (unsigned)pb0 < nblocks_pool ? (unsigned)pb0 : 0u;
         const char *kp = (const char *)a.k_cache + (int64_t)d.g * D * C::EB + (int64_t)pb * blk_bytes;
         const char *vp = (const char *)a.v_cache + (int64_t)d.g * D * C::EB + (int64_t)pb * blk_bytes;
@@ -628,12 +634,12 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(DecodeArgs a)
         };
         // prologue: blocks 0 and 1 in flight (block 0 may already be on its way)
         if (nb_w > 0 && !pre0) {
-            const int p0 = uniform(table[b0 + w]);
+            const int p0 = uniform(unit_block(table, b0 + w));
             issue_k(0, p0);
             issue_v(0, p0);
         }
         if (nb_w > 1) {
-            const int p1 = uniform(table[b0 + w + WAVES]);
+            const int p1 = uniform(unit_block(table, b0 + w + WAVES));
             issue_k(1, p1);
             issue_v(1, p1);
         }
@@ -643,7 +649,7 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(DecodeArgs a)
             ++done_w;
             const int b = b0 + w + WAVES * t;
             const bool more1 = t + 1 < nb_w, more2 = t + 2 < nb_w;  // uniform
-            const int pb2 = more2 ? uniform(table[b + 2 * WAVES]) : 0;
+            const int pb2 = more2 ? uniform(unit_block(table, b + 2 * WAVES)) : 0;
             // K(t); issued after it and possibly in flight: V(t), K(t+1), V(t+1)
             if (more1)
                 wait_vm<NV + NK + NV>();

@@ -243,11 +243,17 @@ __global__ __launch_bounds__(64 * HPG, 2) void decode_hg_kernel(DecodeArgs a)
     const int S = a.num_seqs, Hkv = a.num_kv_heads, Hq = a.num_q_heads, maxB = a.max_blocks;
     const int NHG = Hkv / HPG;  // head groups
     const int PB = a.part_blocks;
+    // the kernel walks 16-token units; a table entry names 2^ts consecutive ones
+    const int ts = a.tbs_log2;
+    const int maxU = maxB << ts;  // units a table row addresses
+    auto unit_block = [&](auto tab, int u) -> int {
+        return (tab[u >> ts] << ts) + (u & ((1 << ts) - 1));
+    };
 
     auto items_of = [&](int L) -> int {
         L = L < 0 ? 0 : L;
         int nb = (L + 15) >> 4;
-        nb = nb > maxB ? maxB : nb;
+        nb = nb > maxU ? maxU : nb;
         return PB > 0 ? (nb + PB - 1) / PB : nb;
     };
 
@@ -359,7 +365,7 @@ __global__ __launch_bounds__(64 * HPG, 2) void decode_hg_kernel(DecodeArgs a)
             L = lens_s[si];
             n = items_of(L);
         }
-        d.L = uniform(L > maxB * 16 ? maxB * 16 : L);
+        d.L = uniform(L > maxU * 16 ? maxU * 16 : L);
         d.n_i = uniform(n);
         const long long rel = it - sbase;
         d.hg = uniform((int)(rel / d.n_i));
@@ -603,8 +609,8 @@ __global__ __launch_bounds__(64 * HPG, 2) void decode_hg_kernel(DecodeArgs a)
     store_q();
     {
         const auto tab = scalar_view(a.block_tables + (int64_t)i * maxB);
-        const int p0 = uniform(tab[sg.b0]);
-        const int p1 = sg.b1 - sg.b0 > 1 ? uniform(tab[sg.b0 + 1]) : p0;
+        const int p0 = uniform(unit_block(tab, sg.b0));
+        const int p1 = sg.b1 - sg.b0 > 1 ? uniform(unit_block(tab, sg.b0 + 1)) : p0;
         const char *kb = head_base(a.k_cache, sg.hg), *vb = head_base(a.v_cache, sg.hg);
         load_k(kr0, kb, p0);
         load_v(vr0, vb, p0);
@@ -656,13 +662,13 @@ __global__ __launch_bounds__(64 * HPG, 2) void decode_hg_kernel(DecodeArgs a)
         // placeholder load of this segment's first block when there is none),
         // so the following segment's loads are already in flight when this one
         // ends.
-        const int p_first = uniform(table[b0]);  // this segment's first block
+        const int p_first = uniform(unit_block(table, b0));  // this segment's first block
         const char *nkbase = kbase, *nvbase = vbase;
         int npb[2] = {p_first, p_first};
         if (has_next) {
             const auto ntab = scalar_view(a.block_tables + (int64_t)i_n * maxB);
-            npb[0] = uniform(ntab[nx.b0]);
-            npb[1] = nx.b1 - nx.b0 > 1 ? uniform(ntab[nx.b0 + 1]) : npb[0];
+            npb[0] = uniform(unit_block(ntab, nx.b0));
+            npb[1] = nx.b1 - nx.b0 > 1 ? uniform(unit_block(ntab, nx.b0 + 1)) : npb[0];
             nkbase = head_base(a.k_cache, nx.hg);
             nvbase = head_base(a.v_cache, nx.hg);
         }
@@ -838,8 +844,8 @@ __global__ __launch_bounds__(64 * HPG, 2) void decode_hg_kernel(DecodeArgs a)
             for (int j = b0 + 2;; j += 2) {
                 const bool more = j < b1;  // uniform
                 const bool more1 = j + 1 < b1;
-                const int p0 = more ? uniform(table[j]) : npb[0];
-                const int p1 = more1 ? uniform(table[j + 1]) : more ? p_first : npb[1];
+                const int p0 = more ? uniform(unit_block(table, j)) : npb[0];
+                const int p1 = more1 ? uniform(unit_block(table, j + 1)) : more ? p_first : npb[1];
                 step(blk0, kr0, vr0, p0, more ? kbase : nkbase, more ? vbase : nvbase);
                 step(blk1, kr1, vr1, p1, more ? kbase : nkbase, more ? vbase : nvbase);
                 if (!more)

@@ -82,10 +82,17 @@ int decode_grid(const pa_shape *s)
     return slot;
 }
 
-// Bytes of one block of one pool: 16 token rows of num_kv_heads x head_dim.
+// Tokens per block (0 in the shape means 16) and the kernels' view of it:
+// every kernel walks 16-token units, block b holding units b * 2^s .. + 2^s - 1.
+int block_size_of(const pa_shape *s) { return s->block_size ? s->block_size : 16; }
+int unit_shift(const pa_shape *s) { return block_size_of(s) == 64 ? 2 : block_size_of(s) == 32 ? 1 : 0; }
+// 16-token units a block table row can address.
+int units_per_seq(const pa_shape *s) { return s->max_blocks_per_seq << unit_shift(s); }
+
+// Bytes of one block of one pool: block_size token rows of num_kv_heads x head_dim.
 int64_t block_bytes_of(const pa_shape *s)
 {
-    return (int64_t)16 * s->num_kv_heads * s->head_dim *
+    return (int64_t)block_size_of(s) * s->num_kv_heads * s->head_dim *
            (s->cache_dtype == PA_F32 ? 4 : s->cache_dtype == PA_BF16 ? 2 : 1);
 }
 
@@ -123,8 +130,10 @@ pa_status check_shape(const pa_shape *s, bool need_tables)
                     s->num_kv_heads);
     if (s->num_blocks <= 0)
         return fail(PA_ERR_INVALID, "num_blocks must be positive");
-    if (s->num_blocks > (int64_t)1 << 31)
-        return fail(PA_ERR_UNSUPPORTED, "num_blocks above 2^31");
+    if (s->block_size != 0 && s->block_size != 16 && s->block_size != 32 && s->block_size != 64)
+        return fail(PA_ERR_UNSUPPORTED, "block_size %d (16, 32 or 64 are built)", s->block_size);
+    if (s->num_blocks * (block_size_of(s) / 16) > (int64_t)1 << 31)
+        return fail(PA_ERR_UNSUPPORTED, "num_blocks * block_size / 16 above 2^31");
     if (need_tables && s->max_blocks_per_seq <= 0)
         return fail(PA_ERR_INVALID, "max_blocks_per_seq must be positive");
     if (s->cache_dtype != PA_F32 && s->cache_dtype != PA_BF16 && s->cache_dtype != PA_FP8_E4M3)
@@ -152,7 +161,7 @@ DecodeLayout decode_layout(const pa_shape *s)
     const int G = s->num_q_heads / s->num_kv_heads;
     const int pb = s->partition_tokens > 0 ? s->partition_tokens / 16 : 0;
     DecodeLayout L;
-    L.slots = pa::decode_partial_slots(s->num_seqs, s->num_kv_heads, G, s->max_blocks_per_seq, pb,
+    L.slots = pa::decode_partial_slots(s->num_seqs, s->num_kv_heads, G, units_per_seq(s), pb,
                                        decode_grid(s));
     L.count_bytes = (size_t)pa::kDecodeCounterSlots * sizeof(int32_t);
     L.ml_bytes = align256((size_t)L.slots * G * 2 * sizeof(float));
@@ -202,7 +211,7 @@ pa_status pa_reshape_and_cache(const void *k, const void *v, void *k_cache, void
     a.v_cache = v_cache;
     a.slot_mapping = slot_mapping;
     a.num_tokens = num_tokens;
-    a.num_slots = shape->num_blocks * 16;
+    a.num_slots = shape->num_blocks * block_size_of(shape);
     a.row_elems = shape->num_kv_heads * shape->head_dim;
     a.src_dtype = src_dtype;
     a.cache_dtype = shape->cache_dtype;
@@ -327,7 +336,8 @@ pa_status pa_decode(float *out, const void *q, const void *k_cache, const void *
     a.num_kv_heads = shape->num_kv_heads;
     a.head_dim = shape->head_dim;
     a.max_blocks = shape->max_blocks_per_seq;
-    a.num_blocks = shape->num_blocks;
+    a.tbs_log2 = unit_shift(shape);
+    a.num_blocks = shape->num_blocks << a.tbs_log2;  // in 16-token units
     a.cache_dtype = shape->cache_dtype;
     a.part_blocks = shape->partition_tokens / 16;
     a.grid = decode_grid(shape);
@@ -403,7 +413,8 @@ pa_status pa_prefill_chunk(float *out, const void *q, const void *k_cache, const
     a.num_kv_heads = shape->num_kv_heads;
     a.head_dim = shape->head_dim;
     a.max_blocks = shape->max_blocks_per_seq;
-    a.num_blocks = shape->num_blocks;
+    a.tbs_log2 = unit_shift(shape);
+    a.num_blocks = shape->num_blocks << a.tbs_log2;  // in 16-token units
     a.cache_dtype = shape->cache_dtype;
     a.kv_splits = kv_splits;
     a.m_tiles = m_tiles;

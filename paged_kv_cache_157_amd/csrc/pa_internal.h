@@ -38,10 +38,12 @@ struct DecodeArgs {
     const void *q;
     const void *k_cache, *v_cache;
     const int32_t *block_tables, *context_lens;
-    int num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks;
-    int64_t num_blocks;
+    int num_seqs, num_q_heads, num_kv_heads, head_dim;
+    int max_blocks;        // width of a block table row (entries)
+    int tbs_log2;          // an entry names 2^tbs_log2 consecutive 16-token units
+    int64_t num_blocks;    // pool size in 16-token units
     int cache_dtype;
-    int part_blocks;       // 0: balanced split; else fixed partitions (blocks)
+    int part_blocks;       // 0: balanced split; else fixed partitions (16-token units)
     int grid;              // persistent work-group count
     float qk_scale;        // softmax scale * log2(e) (* kv_scale for fp8 K)
     float v_scale;         // 1, or kv_scale for fp8 V
@@ -74,8 +76,10 @@ struct PrefillArgs {
     const void *k_cache, *v_cache;
     const int32_t *block_tables, *query_start, *context_lens;
     int64_t total_rows;
-    int num_reqs, num_q_heads, num_kv_heads, head_dim, max_blocks;
-    int64_t num_blocks;
+    int num_reqs, num_q_heads, num_kv_heads, head_dim;
+    int max_blocks;        // width of a block table row (entries)
+    int tbs_log2;          // an entry names 2^tbs_log2 consecutive 16-token units
+    int64_t num_blocks;    // pool size in 16-token units
     int cache_dtype;
     int kv_splits;
     int m_tiles;           // row tiles per (request, KV head), from the largest chunk

@@ -210,7 +210,9 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
         return;
     n = n < a.total_rows - qs ? n : (int)(a.total_rows - qs);
     int Ctx = a.context_lens[r];
-    Ctx = Ctx < 16 * a.max_blocks ? Ctx : 16 * a.max_blocks;  // caller precondition, enforced
+    const int ts = a.tbs_log2;  // a table entry names 2^ts consecutive 16-token units
+    const int maxU = a.max_blocks << ts;
+    Ctx = Ctx < 16 * maxU ? Ctx : 16 * maxU;  // caller precondition, enforced
     const int P = Ctx - n;
     const int pos0 = mt * ppt;
     if (pos0 >= n)
@@ -281,7 +283,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
             const int blk = kt * (KT / 16) + i;
             int e = 0;
             if (blk * 16 < Ctx)  // entries past the context are never read
-                e = tab[blk];
+                e = (tab[blk >> ts] << ts) + (blk & ((1 << ts) - 1));
             pb[i] = (unsigned)e < (unsigned)a.num_blocks ? e : 0;
         }
         const int last = Ctx - 1 - kt * KT;  // last context row of this tile (may exceed KT)

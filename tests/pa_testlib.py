@@ -143,12 +143,13 @@ def to_dev(a: np.ndarray, dtype=None) -> torch.Tensor:
     return t.to("cuda") if dtype is None else t.to("cuda").view(dtype)
 
 
-def random_problem(seed, S, hq, hkv, d, lens, num_blocks, storage, width=None, kv_scale=0.05):
-    """Random decode problem with scattered tables; returns device tensors and
-    host copies of every input."""
+def random_problem(seed, S, hq, hkv, d, lens, num_blocks, storage, width=None, kv_scale=0.05,
+                   block_size=16):
+    """Random decode problem with scattered tables (blocks of block_size
+    tokens); returns device tensors and host copies of every input."""
     rng = np.random.default_rng(seed)
     perm = rng.permutation(num_blocks)
-    nbs = [-(-L // 16) for L in lens]
+    nbs = [-(-L // block_size) for L in lens]
     width = width or max(max(nbs), 1)
     bt = np.full((S, width), -1, np.int32)
     c = 0
@@ -160,7 +161,7 @@ def random_problem(seed, S, hq, hkv, d, lens, num_blocks, storage, width=None, k
     g.manual_seed(seed)
     cdt = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.float8_e4m3fn}[storage]
     qdt = torch.float32 if storage == "f32" else torch.bfloat16
-    shape = (num_blocks, 16, hkv, d)
+    shape = (num_blocks, block_size, hkv, d)
     x = torch.randn(shape, generator=g, device="cuda")
     y = torch.randn(shape, generator=g, device="cuda")
     if storage == "fp8":
@@ -172,7 +173,7 @@ def random_problem(seed, S, hq, hkv, d, lens, num_blocks, storage, width=None, k
     return dict(q=q, k=kc, v=vc, bt=to_dev(bt), lens=to_dev(np.array(lens, np.int32)),
                 bt_h=bt, lens_h=np.array(lens, np.int32), q_h=host_bits(q), k_h=host_bits(kc),
                 v_h=host_bits(vc), scale=1.0 / math.sqrt(d),
-                kv_scale=kv_scale if storage == "fp8" else 1.0, storage=storage)
+                kv_scale=kv_scale if storage == "fp8" else 1.0, storage=storage, bs=block_size)
 
 
 def decode_problem(p, partition_tokens=0):
@@ -185,4 +186,4 @@ def decode_problem(p, partition_tokens=0):
 
 def oracle_problem(p):
     return oracle.decode(p["q_h"], pool_rows(p["k_h"]), pool_rows(p["v_h"]), p["bt_h"],
-                         p["lens_h"], p["scale"], kv_scale=p["kv_scale"])
+                         p["lens_h"], p["scale"], kv_scale=p["kv_scale"], block_size=p["bs"])

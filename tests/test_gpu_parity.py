@@ -300,6 +300,79 @@ def test_partitions_of_many_short_sequences():
 
 
 # ----------------------------------------------------------------------------
+# blocks of 32 and 64 tokens: every kernel walks 16-token units, a table
+# entry naming block_size / 16 consecutive ones
+# ----------------------------------------------------------------------------
+
+BIG_BLOCKS = [(bs, storage, hkv, G, ptok) for bs in (32, 64)
+              for storage, hkv, G, ptok in (("bf16", 2, 7, 0), ("bf16", 8, 4, 0), ("fp8", 8, 4, 512),
+                                            ("fp8", 4, 1, 64), ("f32", 2, 3, 0))]
+
+
+@pytest.mark.parametrize("bs,storage,hkv,G,ptok", BIG_BLOCKS)
+def test_decode_with_larger_blocks(bs, storage, hkv, G, ptok):
+    d = 64 if storage == "f32" else 128
+    lens = [1, bs - 1, bs, bs + 1, 37, 1000, 0, 3 * bs + 5, 2500]
+    nblk = sum(-(-L // bs) for L in lens) + 7
+    say(f"decode block_size={bs} {storage} Hkv={hkv} G={G} ptok={ptok}")
+    p = random_problem(3000 + bs + G, len(lens), G * hkv, hkv, d, lens, nblk, storage,
+                       block_size=bs)
+    got = decode_problem(p, partition_tokens=ptok)
+    assert np.all(got[6] == 0.0)
+    assert max_err(got, oracle_problem(p)) <= TOL[storage]
+
+
+@pytest.mark.parametrize("bs", [32, 64])
+@pytest.mark.parametrize("storage", ["bf16", "fp8"])
+def test_prefill_with_larger_blocks(bs, storage):
+    hc = [(0, 77), (500, 100), (bs, 1)]
+    lens = [h + n for h, n in hc]
+    p = random_problem(3100 + bs, len(hc), 32, 8, 128, lens,
+                       sum(-(-L // bs) for L in lens) + 3, storage, block_size=bs)
+    qs = np.concatenate([[0], np.cumsum([n for _, n in hc])]).astype(np.int32)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(3200 + bs)
+    qp = torch.randn((int(qs[-1]), 32, 128), generator=g, device="cuda").to(torch.bfloat16)
+    out = torch.full(qp.shape, float("nan"), dtype=torch.float32, device="cuda")
+    binding.prefill_chunk(out, qp, p["k"], p["v"], p["bt"], to_dev(qs), p["lens"], p["scale"],
+                          kv_scale=p["kv_scale"])
+    torch.cuda.synchronize()
+    ref = oracle.prefill(host_bits(qp), pool_rows(p["k_h"]), pool_rows(p["v_h"]), p["bt_h"], qs,
+                         p["lens_h"], p["scale"], kv_scale=p["kv_scale"], block_size=bs)
+    assert max_err(out.cpu().numpy(), ref) <= TOL[storage]
+
+
+@pytest.mark.parametrize("bs", [32, 64])
+def test_cache_write_and_copies_with_larger_blocks(bs):
+    nblk, hkv, d = 50, 4, 128
+    g = torch.Generator(device="cuda")
+    g.manual_seed(3300 + bs)
+    kc = torch.randn((nblk, bs, hkv, d), generator=g, device="cuda").to(torch.bfloat16)
+    vc = torch.randn((nblk, bs, hkv, d), generator=g, device="cuda").to(torch.bfloat16)
+    T = 70
+    kn = torch.randn((T, hkv, d), generator=g, device="cuda").to(torch.bfloat16)
+    vn = torch.randn((T, hkv, d), generator=g, device="cuda").to(torch.bfloat16)
+    rng = np.random.default_rng(3400 + bs)
+    slots = rng.choice(nblk * bs, T, replace=False).astype(np.int64)
+    slots[3] = -1  # padding: skipped
+    kh, vh = pool_rows(host_bits(kc)).copy(), pool_rows(host_bits(vc)).copy()
+    oracle.reshape_and_cache(host_bits(kn), host_bits(vn), kh, vh, slots)
+    binding.reshape_and_cache(kn, vn, kc, vc, to_dev(slots))
+    pairs = np.stack([rng.permutation(25), 25 + rng.permutation(25)], 1).astype(np.int64)
+    oracle.copy_blocks(kh, vh, pairs, block_size=bs)
+    binding.copy_blocks(kc, vc, to_dev(pairs))
+    hk = torch.zeros((10, bs, hkv, d), dtype=torch.bfloat16).pin_memory()
+    hv = torch.zeros_like(hk).pin_memory()
+    out_pairs = np.stack([rng.permutation(nblk)[:10], np.arange(10)], 1).astype(np.int64)
+    hkh, hvh = pool_rows(host_bits(hk)).copy(), pool_rows(host_bits(hv)).copy()
+    oracle.swap_blocks(kh, vh, hkh, hvh, out_pairs, block_size=bs)
+    binding.swap_blocks(kc, vc, hk, hv, to_dev(out_pairs))
+    torch.cuda.synchronize()
+    assert np.array_equal(pool_rows(host_bits(kc)), kh) and np.array_equal(pool_rows(host_bits(vc)), vh)
+    assert np.array_equal(pool_rows(host_bits(hk)), hkh) and np.array_equal(pool_rows(host_bits(hv)), hvh)
+
+
+# ----------------------------------------------------------------------------
 # copy-on-write block copies: bit-exact against the oracle's copy
 # ----------------------------------------------------------------------------
 

@@ -429,6 +429,41 @@ def test_copy_blocks_skips_ids_outside_the_pool():
     assert np.array_equal(kp[:48], k0[:48]) and np.array_equal(vp[:48], v0[:48])
 
 
+@pytest.mark.parametrize("B", [32, 64])
+def test_larger_blocks_address_the_same_slots(B):
+    """[L33] §2.2 with B tokens per block: token t sits at table[t // B] * B
+    + t % B.  The same pool seen as 16-token blocks, every B-block entry p
+    becoming entries p*B/16 .. p*B/16 + B/16 - 1, holds every token at the
+    same slot, so both views give the same bits."""
+    rng = np.random.default_rng(15)
+    f = B // 16
+    lens = [1, B - 1, B, B + 1, 5 * B + 7]
+    c = random_case(rng, len(lens), 8, 2, 64, lens, 40 * f, "bf16")  # 16-slot view
+    nb = [-(-L // B) for L in lens]
+    perm = rng.permutation(40)
+    bt = np.full((len(lens), max(nb)), -1, np.int32)
+    k = 0
+    for i, n in enumerate(nb):
+        bt[i, :n] = perm[k:k + n]
+        k += n
+    bt16 = np.full((len(lens), max(nb) * f), -1, np.int32)
+    for i, n in enumerate(nb):
+        for j in range(n):
+            bt16[i, j * f:(j + 1) * f] = bt[i, j] * f + np.arange(f)
+    a = oracle.decode(c["q"], c["kpool"], c["vpool"], bt, c["lens"], 0.125, block_size=B)
+    b = oracle.decode(c["q"], c["kpool"], c["vpool"], bt16, c["lens"], 0.125)
+    assert np.array_equal(a, b)
+    # token 37 with B = 32: logical block 1, offset 5
+    if B == 32:
+        q = np.zeros((1, 1, 64), np.float32)
+        k1 = np.zeros((40 * 32, 1, 64), np.float32)
+        v1 = np.zeros_like(k1)
+        v1[9 * 32 + 5, 0] = 1.0
+        out = oracle.decode(q, k1, v1, np.array([[3, 9]], np.int32), np.array([38], np.int32), 1.0,
+                            block_size=32)
+        np.testing.assert_allclose(out[0, 0], np.full(64, 1.0 / 38), rtol=0, atol=1e-15)
+
+
 def test_unused_table_entries_are_never_read():
     rng = np.random.default_rng(8)
     c = random_case(rng, 2, 4, 2, 64, [17, 40], 8, "bf16")
