@@ -193,7 +193,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
     constexpr float TAU = 8.0f;
     __shared__ PrefillSmem<CDT, D> sm;
 
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, w = uniform(tid >> 6);
     const int hl = lane >> 5, col = lane & 31;
     const int KS = a.kv_splits, Hq = a.num_q_heads, Hkv = a.num_kv_heads, G = Hq / Hkv;
     int b = blockIdx.x;
@@ -276,15 +276,44 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
         const int ch = C::RAW ? slot : slot ^ (isv ? swz_v<D>(row) : swz_k<D>(row));
         doff[j] = (uint32_t)((row & 15) * tok_bytes + ch * 16);
     }
-    auto issue_tile = [&](int kt, int s) {
-        int pb[4];
+    // 16-token units holding context (>= 1 whenever a tile is issued)
+    const int ctx_units = (Ctx + 15) >> 4;
+    // physical block entry of 16-token unit kb of tile kt (units past the
+    // context take the last one's entry; no row of theirs is fetched)
+    auto unit_entry = [&](int kt, int kb) -> int {
+        int blk = kt * (KT / 16) + kb;
+        blk = blk < ctx_units ? blk : ctx_units - 1;
+        const int e = (tab[blk >> ts] << ts) + (blk & ((1 << ts) - 1));
+        return (unsigned)e < (unsigned)a.num_blocks ? e : 0;
+    };
+    // Instruction j of this wave always moves rows of the same unit of a tile
+    // (DMA_ROWS divides 16).  With two or more instructions per wave, K
+    // instruction j and V instruction j + DPW / 2 move the same rows, so a wave
+    // needs the entries of DPW / 2 units; with one, of one unit.  The table
+    // entries are read here and used by issue_tile, so their loads go out back
+    // to back and are waited for only where the entries are needed.
+    static_assert((DPW == 1 || DPW % 2 == 0) && C::DMA_TILE == C::WAVES * DPW, "DMA layout");
+    constexpr int NU = DPW >= 2 ? DPW / 2 : 1;
+    struct Units {
+        int blk[NU], raw[NU];
+    };
+    auto tile_units = [&](int kt, Units &un) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int blk = kt * (KT / 16) + i;
-            int e = 0;
-            if (blk * 16 < Ctx)  // entries past the context are never read
-                e = (tab[blk >> ts] << ts) + (blk & ((1 << ts) - 1));
-            pb[i] = (unsigned)e < (unsigned)a.num_blocks ? e : 0;
+        for (int j = 0; j < NU; ++j) {
+            const int i = w + C::WAVES * j;
+            const int ii = DPW >= 2 || i < C::DMA_TILE / 2 ? i : i - C::DMA_TILE / 2;
+            int blk = kt * (KT / 16) + ((ii * C::DMA_ROWS) >> 4);
+            blk = blk < ctx_units ? blk : ctx_units - 1;
+            un.blk[j] = blk;
+            un.raw[j] = tab[blk >> ts];
+        }
+    };
+    auto issue_tile = [&](int kt, int s, const Units &un) {
+        int pb[NU];
+#pragma unroll
+        for (int j = 0; j < NU; ++j) {
+            const int e = (un.raw[j] << ts) + (un.blk[j] & ((1 << ts) - 1));
+            pb[j] = (unsigned)e < (unsigned)a.num_blocks ? e : 0;
         }
         const int last = Ctx - 1 - kt * KT;  // last context row of this tile (may exceed KT)
 #pragma unroll
@@ -298,14 +327,15 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
             const int row0 = ii * C::DMA_ROWS;
             if (row0 + C::DMA_ROWS - 1 <= last) {
                 // whole instruction inside the context: one block, scalar base
-                const int kb = row0 >> 4;
-                const int p = kb == 0 ? pb[0] : kb == 1 ? pb[1] : kb == 2 ? pb[2] : pb[3];
-                dma16(base + (int64_t)p * 16 * tok_bytes + doff[j], dst);
+                dma16(base + (int64_t)pb[j % NU] * 16 * tok_bytes + doff[j], dst);
             } else {
+                // the context ends inside this instruction (last tile only)
+                const int p0 = unit_entry(kt, 0), p1 = unit_entry(kt, 1);
+                const int p2 = unit_entry(kt, 2), p3 = unit_entry(kt, 3);
                 const int row = row0 + lane / SPR, slot = lane % SPR;
                 const int key = row < last ? row : last;
                 const int kb = key >> 4;
-                const int p = kb == 0 ? pb[0] : kb == 1 ? pb[1] : kb == 2 ? pb[2] : pb[3];
+                const int p = kb == 0 ? p0 : kb == 1 ? p1 : kb == 2 ? p2 : p3;
                 const int ch = C::RAW ? slot : slot ^ (isv ? swz_v<D>(row) : swz_k<D>(row));
                 dma16(base + ((int64_t)p * 16 + (key & 15)) * tok_bytes + ch * 16, dst);
             }
@@ -472,24 +502,38 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
     };
     using Mode0 = std::integral_constant<int, 0>;
     using Mode1 = std::integral_constant<int, 1>;
+    // The table entries of the next tile to issue are read one iteration ahead,
+    // at the end of the compute: the barrier's wait then covers their latency
+    // instead of every wave stalling on them right after it.
+    Units pbn = {};
     if constexpr (!C::RAW) {
         // the ring stages are the compute tiles
-        for (int u = 0; u < NS - 1 && u < nt; ++u)
-            issue_tile(t0 + u, u);
+        for (int u = 0; u < NS - 1 && u < nt; ++u) {
+            tile_units(t0 + u, pbn);
+            issue_tile(t0 + u, u, pbn);
+        }
+        if (NS - 1 < nt)
+            tile_units(t0 + NS - 1, pbn);
         for (int u = 0; u < nt; ++u) {
             const int kt = t0 + u;
             const int ahead = nt - 1 - u < NS - 2 ? nt - 1 - u : NS - 2;
             wait_tiles_in_flight<DPW>(ahead);  // tile u landed
             barrier_lds();  // tile u visible to all; stage (u - 1) % NS is free
             if (u + NS - 1 < nt)
-                issue_tile(kt + NS - 1, (u + NS - 1) % NS);
+                issue_tile(kt + NS - 1, (u + NS - 1) % NS, pbn);
             const char *st_lds = sm.ring + (u % NS) * C::STAGEB;
             compute_tile(st_lds, st_lds + C::TILEB, kt, Mode0{});
+            if (u + NS < nt)
+                tile_units(kt + NS, pbn);
         }
     } else {
         // raw ring -> widened double buffer, one tile ahead of the compute
-        for (int u = 0; u < NS - 1 && u < nt; ++u)
-            issue_tile(t0 + u, u);
+        for (int u = 0; u < NS - 1 && u < nt; ++u) {
+            tile_units(t0 + u, pbn);
+            issue_tile(t0 + u, u, pbn);
+        }
+        if (NS - 1 < nt)
+            tile_units(t0 + NS - 1, pbn);
         if (nt > 0) {
             wait_tiles_in_flight<DPW>(nt - 1 < NS - 2 ? nt - 1 : NS - 2);
             barrier_lds();
@@ -503,11 +547,13 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
             }
             barrier_lds();  // widened tile u visible; raw stage of tile u - 1 is free
             if (u + NS - 1 < nt)
-                issue_tile(kt + NS - 1, (u + NS - 1) % NS);
+                issue_tile(kt + NS - 1, (u + NS - 1) % NS, pbn);
             const char *cb_lds = sm.ring + NS * C::STAGEB + (u & 1) * 2 * C::TILEB;
             compute_tile(cb_lds, cb_lds + C::TILEB, kt, Mode1{});
             if (u + 1 < nt)
                 widen_tile((u + 1) % NS, (u + 1) & 1);
+            if (u + NS < nt)
+                tile_units(kt + NS, pbn);
         }
     }
 
