@@ -112,6 +112,21 @@ __device__ __forceinline__ int swz_v(int key)
     return D == 128 ? 4 * j + 2 * (j >> 1) : 2 * j;
 }
 
+// max / sum of the values of lanes l and l ^ 32: gfx950's lane swap exchanges
+// the two halves of the wave in registers; swapping a value with itself leaves
+// {v(l), v(l ^ 32)} in the two results of every lane (in an order that depends
+// on the half, hence only symmetric combinations).
+__device__ __forceinline__ float max_halves(float v)
+{
+    const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(h[0]), __uint_as_float(h[1]));
+}
+__device__ __forceinline__ float sum_halves(float v)
+{
+    const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(h[0]) + __uint_as_float(h[1]);
+}
+
 // Compile-time loop: f(std::integral_constant<int, 0>), ..., f(<N - 1>).
 template <typename F, int... I>
 __device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, I...>)
@@ -374,16 +389,39 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
         vofs[dt] = (4 * hl + jv) * ROWB + ((4 * dt + 2 * qd + (mv >> 1)) ^ fv) * 16 + (mv & 1) * 8;
 
     // ---- S^T = K Q^T of one tile (both 32-key halves) -------------------------------
+    // K fragments are read two 16-d steps ahead of their products, so the LDS
+    // latency of a step overlaps the products of the two before it
     auto s_tile = [&](const char *kt_lds, f32x16 (&s)[2]) {
+        constexpr int AH = ST < 3 ? ST : 3;  // steps of fragments in flight
+        u32x4 ka[AH][2];
+        auto read = [&](int st) {
+#pragma unroll
+            for (int kc = 0; kc < 2; ++kc)
+                ka[st % AH][kc] = *(const u32x4 *)(kt_lds + kc * 32 * ROWB + kofs[st]);
+        };
         s[0] = f32x16{};
         s[1] = f32x16{};
 #pragma unroll
-        for (int st = 0; st < ST; ++st)
+        for (int st = 0; st < AH - 1; ++st)
+            read(st);
 #pragma unroll
-            for (int kc = 0; kc < 2; ++kc) {
-                const u32x4 ka = *(const u32x4 *)(kt_lds + kc * 32 * ROWB + kofs[st]);
-                s[kc] = mfma32(ka, qb[st], s[kc]);
-            }
+        for (int st = 0; st < ST; ++st) {
+            if (st + AH - 1 < ST)
+                read(st + AH - 1);
+#pragma unroll
+            for (int kc = 0; kc < 2; ++kc)
+                s[kc] = mfma32(ka[st % AH][kc], qb[st], s[kc]);
+        }
+        // keep that order through scheduling (which would otherwise sink each
+        // read to its product to save registers): the first reads, then per
+        // step two products and the reads of a later step
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * (AH - 1), 0);
+        static_for<ST>([&](auto st_) {
+            constexpr int st = decltype(st_)::value;
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+            if constexpr (st + AH - 1 < ST)
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        });
     };
     // ---- mask (diagonal / ragged tiles only), row maximum, lazy rescale --------------
     // Raises the running maximum when the tile exceeds it by more than TAU
@@ -407,7 +445,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
 #pragma unroll
             for (int i = 0; i < 16; ++i)
                 tm = fmaxf(tm, s[kc][i]);
-        tm = fmaxf(tm, __shfl_xor(tm, 32)) * c;  // c > 0: scaled maximum
+        tm = max_halves(tm) * c;  // c > 0: scaled maximum
         if (wave_any(tm > mref + TAU)) {
             const float mnew = fmaxf(mref, tm);
             const float alpha = mnew == -INFINITY ? 1.f : fast_exp2(mref - mnew);
@@ -558,7 +596,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
     }
 
     // ---- finish: row sums, then normalise or store a partial ------------------
-    lsum += __shfl_xor(lsum, 32);
+    lsum = sum_halves(lsum);
     if (hl == 0) {
         sm.ml[w][0][col] = mref;
         sm.ml[w][1][col] = lsum;
