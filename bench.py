@@ -324,12 +324,12 @@ def main():
         del hk, hv, flat_d, flat_h
 
     # block-size trade-off ([L33] §2.2, appendix Q3): the batch's lengths
-    # decoded from pools of 16-, 32- and 64-token blocks, scattered at random
+    # decoded from pools of 8-, 16-, 32- and 64-token blocks, scattered at random
     bs_res = None
     if args.extras and cfg.cache_dtype == "bf16":
         bs_res = {}
         L = step.plan.context_lens.astype(np.int64)
-        for B in (16, 32, 64):
+        for B in (8, 16, 32, 64):
             nbs = (L + B - 1) // B
             nblk = int(nbs.sum()) + 64
             rng = np.random.default_rng(cfg.seed + B)

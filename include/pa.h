@@ -76,10 +76,11 @@ typedef struct {
     int32_t partition_tokens;   /* decode split-K: 0 = balanced split over the whole
                                    GPU, else fixed partitions of this many tokens
                                    (a multiple of 16)                               */
-    int32_t block_size;         /* tokens per block: 16 (0 also means 16), 32 or 64;
-                                   [L33] §2.2: token t of a sequence lives in slot
+    int32_t block_size;         /* tokens per block: 8, 16 (0 also means 16), 32 or
+                                   64; [L33] §2.2: token t of a sequence lives in slot
                                    table[t / block_size] * block_size
-                                   + t % block_size                                  */
+                                   + t % block_size.  With 8, decode always runs the
+                                   one-KV-head kernel                                */
 } pa_shape;
 
 /*

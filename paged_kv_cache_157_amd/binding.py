@@ -108,9 +108,9 @@ def _require(t: torch.Tensor, name: str, device: torch.device, dtype=None, ndim=
 
 def make_shape(q_heads: int, k_cache: torch.Tensor, q_dtype: torch.dtype, num_seqs: int,
                max_blocks: int, kv_scale: float = 1.0, partition_tokens: int = 0) -> PAShape:
-    if k_cache.dim() != 4 or k_cache.shape[1] not in (16, 32, 64):
+    if k_cache.dim() != 4 or k_cache.shape[1] not in (8, 16, 32, 64):
         raise ValueError("KV pools must be [num_blocks, block_size, num_kv_heads, head_dim] "
-                         "with block_size 16, 32 or 64")
+                         "with block_size 8, 16, 32 or 64")
     if k_cache.dtype not in _DTYPES or q_dtype not in _DTYPES:
         raise ValueError(f"unsupported dtypes {q_dtype} / {k_cache.dtype}")
     return PAShape(num_seqs=num_seqs, num_q_heads=q_heads, num_kv_heads=k_cache.shape[2],

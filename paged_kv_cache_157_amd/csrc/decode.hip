@@ -217,7 +217,9 @@ __device__ __forceinline__ void dma16(const void *src, void *lds_dst)
     __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)lds_dst, 16, 0, 0);
 }
 
-template <int CDT, int D, int G, int NSTAGE, int WAVES>
+// H8: the pools hold 8-token blocks (tbs_log2 < 0; a separate instantiation, so
+// that the address arithmetic of larger blocks carries no branch for it)
+template <int CDT, int D, int G, int NSTAGE, int WAVES, bool H8>
 __global__ __launch_bounds__(64 * WAVES) void decode_kernel(DecodeArgs a)
 {
     using C = DecodeCfg<CDT, D, G>;
@@ -236,11 +238,26 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(DecodeArgs a)
     const int w = uniform(tid >> 6);
     const int S = a.num_seqs, Hkv = a.num_kv_heads, Hq = a.num_q_heads, maxB = a.max_blocks;
     const int PB = a.part_blocks;
-    // the kernel walks 16-token units; a table entry names 2^ts consecutive ones
+    // The kernel walks 16-token units.  With blocks of 16 or more tokens a
+    // table entry names 2^ts consecutive units (ts >= 0); with 8-token blocks
+    // (ts < 0) a unit is two blocks, tab[2u] and tab[2u + 1], whose rows sit
+    // in two unrelated places: each lane then takes the base of the half that
+    // holds its row.
     const int ts = a.tbs_log2;
-    const int maxU = maxB << ts;  // units a table row addresses
-    auto unit_block = [&](auto tab, int u) -> int {
-        return (tab[u >> ts] << ts) + (u & ((1 << ts) - 1));
+    constexpr bool h8 = H8;
+    const int maxU = h8 ? (maxB + 1) >> 1 : maxB << ts;  // units a table row addresses
+    const int maxL = h8 ? 8 * maxB : 16 * maxU;          // tokens a table row addresses
+    // physical location of unit u: {unit index, -} or {block of rows 0-7, of rows 8-15}
+    struct Phys {
+        int a, b;
+    };
+    auto unit_block = [&](auto tab, int u) -> Phys {
+        if (h8) {
+            const int e1 = 2 * u + 1 < maxB ? 2 * u + 1 : maxB - 1;  // rows past the table are masked
+            return Phys{tab[2 * u], tab[e1]};
+        }
+        const int e = (tab[u >> ts] << ts) + (u & ((1 << ts) - 1));
+        return Phys{e, e};
     };
 
     auto items_of = [&](int L) -> int {
@@ -410,7 +427,23 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(DecodeArgs a)
 
     const int64_t tok_bytes = (int64_t)Hkv * D * C::EB;
     const int64_t blk_bytes = 16 * tok_bytes;
-    const unsigned nblocks_pool = (unsigned)a.num_blocks;
+    const int64_t half_bytes = 8 * tok_bytes;
+    const unsigned nblocks_pool = (unsigned)a.num_blocks;  // units, or 8-token blocks
+    // Base address of a lane's row, given the pool base of its KV head and the
+    // lane's offset inside a 16-token unit (its row is in the upper half iff
+    // off >= 8 rows: the column part of off is less than one row).  Out-of-range
+    // entries read block 0 (caller precondition; keeps every access in the pool).
+    auto row_addr = [&](const char *hbase, Phys p, unsigned off) -> const char * {
+        if (!h8) {
+            const unsigned u = (unsigned)p.a < nblocks_pool ? (unsigned)p.a : 0u;
+            return hbase + (int64_t)u * blk_bytes + off;
+        }
+        const unsigned b0 = (unsigned)p.a < nblocks_pool ? (unsigned)p.a : 0u;
+        const unsigned b1 = (unsigned)p.b < nblocks_pool ? (unsigned)p.b : 0u;
+        const char *lo = hbase + (int64_t)b0 * half_bytes;
+        const char *hi = hbase + (int64_t)b1 * half_bytes - half_bytes;
+        return (off >= (unsigned)half_bytes ? hi : lo) + off;
+    };
 
     // per-lane byte offsets of the K and V chunks this lane fetches inside one
     // block (KV head 0); the DMA puts chunk (j, c) of lane l at LDS
@@ -447,7 +480,7 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(DecodeArgs a)
             L = lens_s[si];
             n = items_of(L);
         }
-        d.L = uniform(L > maxU * 16 ? maxU * 16 : L);
+        d.L = uniform(L > maxL ? maxL : L);
         d.n_i = uniform(n);
         const long long rel = it - sbase;
         d.g = uniform((int)(rel / d.n_i));
@@ -489,18 +522,19 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(DecodeArgs a)
     auto issue_first = [&](int si, const Seg &d) -> bool {
         if (d.b0 + w >= d.b1)
             return false;
-        const int pb0 = uniform(unit_block(scalar_view(a.block_tables + (int64_t)si * maxB), d.b0 + w));
-        const unsigned pb = (unsigned)pb0 < nblocks_pool ? (unsigned)pb0 : 0u;
-        const char *kp = (const char *)a.k_cache + (int64_t)d.g * D * C::EB + (int64_t)pb * blk_bytes;
-        const char *vp = (const char *)a.v_cache + (int64_t)d.g * D * C::EB + (int64_t)pb * blk_bytes;
+        Phys pb = unit_block(scalar_view(a.block_tables + (int64_t)si * maxB), d.b0 + w);
+        pb.a = uniform(pb.a);
+        pb.b = uniform(pb.b);
+        const char *kh = (const char *)a.k_cache + (int64_t)d.g * D * C::EB;
+        const char *vh = (const char *)a.v_cache + (int64_t)d.g * D * C::EB;
 #pragma unroll
         for (int j = 0; j < ROUNDS; ++j)
 #pragma unroll
             for (int c = 0; c < CPL; ++c)
-                dma16(kp + (size_t)koff[j][c], my_ring + (j * CPL + c) * 1024);
+                dma16(row_addr(kh, pb, koff[j][c]), my_ring + (j * CPL + c) * 1024);
 #pragma unroll
         for (int v = 0; v < VPASS; ++v)
-            dma16(vp + (size_t)voff[v], my_ring + KB + v * 1024);
+            dma16(row_addr(vh, pb, voff[v]), my_ring + KB + v * 1024);
         return true;
     };
 
@@ -614,32 +648,32 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(DecodeArgs a)
         // of block t's stage as soon as QK(t) is done, V of block t + 2 into the
         // V half once PV(t) is done, so about 1.5 blocks stay in flight per wave.
         constexpr int NK = ROUNDS * CPL, NV = VPASS;  // DMA instructions per block (K, V)
-        auto issue_k = [&](int t, int pb) {
-            pb = (unsigned)pb < nblocks_pool ? pb : 0;
-            const char *kp = kbase + (int64_t)pb * blk_bytes;
+        auto issue_k = [&](int t, Phys pb) {
             uint8_t *st = my_ring + (t & 1) * 2 * KB;
 #pragma unroll
             for (int j = 0; j < ROUNDS; ++j)
 #pragma unroll
                 for (int c = 0; c < CPL; ++c)
-                    dma16(kp + (size_t)koff[j][c], st + (j * CPL + c) * 1024);
+                    dma16(row_addr(kbase, pb, koff[j][c]), st + (j * CPL + c) * 1024);
         };
-        auto issue_v = [&](int t, int pb) {
-            pb = (unsigned)pb < nblocks_pool ? pb : 0;
-            const char *vp = vbase + (int64_t)pb * blk_bytes;
+        auto issue_v = [&](int t, Phys pb) {
             uint8_t *st = my_ring + (t & 1) * 2 * KB;
 #pragma unroll
             for (int v = 0; v < VPASS; ++v)
-                dma16(vp + (size_t)voff[v], st + KB + v * 1024);
+                dma16(row_addr(vbase, pb, voff[v]), st + KB + v * 1024);
+        };
+        auto unit_u = [&](int u) -> Phys {
+            Phys p = unit_block(table, u);
+            return Phys{uniform(p.a), uniform(p.b)};
         };
         // prologue: blocks 0 and 1 in flight (block 0 may already be on its way)
         if (nb_w > 0 && !pre0) {
-            const int p0 = uniform(unit_block(table, b0 + w));
+            const Phys p0 = unit_u(b0 + w);
             issue_k(0, p0);
             issue_v(0, p0);
         }
         if (nb_w > 1) {
-            const int p1 = uniform(unit_block(table, b0 + w + WAVES));
+            const Phys p1 = unit_u(b0 + w + WAVES);
             issue_k(1, p1);
             issue_v(1, p1);
         }
@@ -649,7 +683,7 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(DecodeArgs a)
             ++done_w;
             const int b = b0 + w + WAVES * t;
             const bool more1 = t + 1 < nb_w, more2 = t + 2 < nb_w;  // uniform
-            const int pb2 = more2 ? uniform(unit_block(table, b + 2 * WAVES)) : 0;
+            const Phys pb2 = more2 ? unit_u(b + 2 * WAVES) : Phys{0, 0};
             // K(t); issued after it and possibly in flight: V(t), K(t+1), V(t+1)
             if (more1)
                 wait_vm<NV + NK + NV>();
@@ -1004,20 +1038,20 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(DecodeArgs a)
     }
 }
 
-int decode_hpg(int num_kv_heads, int group)
+int decode_hpg(int num_kv_heads, int group, int tbs_log2)
 {
-    return num_kv_heads % 4 == 0 && num_kv_heads >= 8 && group >= 2 ? 4 : 1;
+    return num_kv_heads % 4 == 0 && num_kv_heads >= 8 && group >= 2 && tbs_log2 >= 0 ? 4 : 1;
 }
 
 int64_t decode_partial_slots(int num_seqs, int num_kv_heads, int group, int max_blocks,
-                             int part_blocks, int grid)
+                             int part_blocks, int grid, int tbs_log2)
 {
     const int64_t pairs = (int64_t)num_seqs * num_kv_heads;
     if (part_blocks > 0)  // one record per (partition, sequence, KV head)
         return pairs * ((max_blocks + part_blocks - 1) / part_blocks);
     // balanced split: a record per (range, sequence, KV head) that a range
     // can start a segment of, times the heads of one work-group
-    const int hpg = decode_hpg(num_kv_heads, group);
+    const int hpg = decode_hpg(num_kv_heads, group, tbs_log2);
     return ((int64_t)grid + pairs / hpg) * hpg;
 }
 
@@ -1035,50 +1069,52 @@ bool decode_supported(int cache_dtype, int head_dim, int group)
 }
 
 template <int CDT, int D, int G>
-static DecodeKernels kernels_t()
+static DecodeKernels kernels_t(bool h8)
 {
-    return DecodeKernels{(const void *)decode_kernel<CDT, D, G, DECODE_STAGES, DECODE_WAVES>,
+    return DecodeKernels{h8 ? (const void *)decode_kernel<CDT, D, G, DECODE_STAGES, DECODE_WAVES, true>
+                            : (const void *)decode_kernel<CDT, D, G, DECODE_STAGES, DECODE_WAVES, false>,
                          64 * DECODE_WAVES};
 }
 
 template <int CDT, int D>
-static DecodeKernels kernels_d(int G)
+static DecodeKernels kernels_d(int G, bool h8)
 {
     switch (G) {
-    case 1: return kernels_t<CDT, D, 1>();
-    case 2: return kernels_t<CDT, D, 2>();
-    case 3: return kernels_t<CDT, D, 3>();
-    case 4: return kernels_t<CDT, D, 4>();
-    case 5: return kernels_t<CDT, D, 5>();
-    case 6: return kernels_t<CDT, D, 6>();
-    case 7: return kernels_t<CDT, D, 7>();
-    default: return kernels_t<CDT, D, 8>();
+    case 1: return kernels_t<CDT, D, 1>(h8);
+    case 2: return kernels_t<CDT, D, 2>(h8);
+    case 3: return kernels_t<CDT, D, 3>(h8);
+    case 4: return kernels_t<CDT, D, 4>(h8);
+    case 5: return kernels_t<CDT, D, 5>(h8);
+    case 6: return kernels_t<CDT, D, 6>(h8);
+    case 7: return kernels_t<CDT, D, 7>(h8);
+    default: return kernels_t<CDT, D, 8>(h8);
     }
 }
 
-DecodeKernels decode_kernels(int cache_dtype, int head_dim, int group, int hpg)
+DecodeKernels decode_kernels(int cache_dtype, int head_dim, int group, int hpg, bool h8)
 {
     if (hpg == 4)
         return decode_hg4_kernels(cache_dtype, head_dim, group);
     if (cache_dtype == DT_F32)
-        return kernels_d<DT_F32, 64>(group);
+        return kernels_d<DT_F32, 64>(group, h8);
     if (cache_dtype == DT_BF16)
-        return head_dim == 64 ? kernels_d<DT_BF16, 64>(group) : kernels_d<DT_BF16, 128>(group);
+        return head_dim == 64 ? kernels_d<DT_BF16, 64>(group, h8) : kernels_d<DT_BF16, 128>(group, h8);
     if (head_dim == 64) {
         switch (group) {
-        case 1: return kernels_t<DT_FP8, 64, 1>();
-        case 2: return kernels_t<DT_FP8, 64, 2>();
-        case 3: return kernels_t<DT_FP8, 64, 3>();
-        default: return kernels_t<DT_FP8, 64, 4>();
+        case 1: return kernels_t<DT_FP8, 64, 1>(h8);
+        case 2: return kernels_t<DT_FP8, 64, 2>(h8);
+        case 3: return kernels_t<DT_FP8, 64, 3>(h8);
+        default: return kernels_t<DT_FP8, 64, 4>(h8);
         }
     }
-    return kernels_d<DT_FP8, 128>(group);
+    return kernels_d<DT_FP8, 128>(group, h8);
 }
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream)
 {
     const int G = a.num_q_heads / a.num_kv_heads;
-    const DecodeKernels k = decode_kernels(a.cache_dtype, a.head_dim, G, decode_hpg(a.num_kv_heads, G));
+    const DecodeKernels k = decode_kernels(a.cache_dtype, a.head_dim, G,
+                                           decode_hpg(a.num_kv_heads, G, a.tbs_log2), a.tbs_log2 < 0);
     DecodeArgs args = a;
     void *params[] = {&args};
     return hipLaunchKernel(k.main, dim3(a.grid), dim3(k.threads), params, 0, stream);

@@ -55,24 +55,45 @@ int device_cus()
     return cached[dev];
 }
 
+// Tokens per block (0 in the shape means 16) and the kernels' view of it:
+// every kernel walks 16-token units, block b holding units b * 2^s .. + 2^s - 1;
+// s = -1 for 8-token blocks, where a unit is the two blocks of entries 2u, 2u + 1.
+int block_size_of(const pa_shape *s) { return s->block_size ? s->block_size : 16; }
+int unit_shift(const pa_shape *s)
+{
+    const int b = block_size_of(s);
+    return b == 64 ? 2 : b == 32 ? 1 : b == 8 ? -1 : 0;
+}
+// 16-token units a block table row can address.
+int units_per_seq(const pa_shape *s)
+{
+    return unit_shift(s) < 0 ? (s->max_blocks_per_seq + 1) / 2 : s->max_blocks_per_seq << unit_shift(s);
+}
+// Pool size as the kernels count it: 16-token units, or 8-token blocks.
+int64_t kernel_blocks(const pa_shape *s)
+{
+    return unit_shift(s) < 0 ? s->num_blocks : s->num_blocks << unit_shift(s);
+}
+
 // Persistent decode grid: as many work-groups as can be resident at once
 // (compute units x occupancy of the kernel that serves this shape), so every
 // work-group of the balanced split runs concurrently.
 int decode_grid(const pa_shape *s)
 {
     static std::mutex mu;
-    static int cached[64][3][2][9][2] = {};
+    static int cached[64][3][2][9][3] = {};
     const int G = s->num_q_heads / s->num_kv_heads;
-    const int hpg = pa::decode_hpg(s->num_kv_heads, G);
+    const int hpg = pa::decode_hpg(s->num_kv_heads, G, unit_shift(s));
     const int dt = s->cache_dtype, dh = s->head_dim == 128 ? 1 : 0;
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
         return 256;
     std::lock_guard<std::mutex> lock(mu);
-    int &slot = cached[dev][dt][dh][G][hpg == 4];
+    const bool h8 = unit_shift(s) < 0;
+    int &slot = cached[dev][dt][dh][G][hpg == 4 ? 1 : h8 ? 2 : 0];
     if (slot == 0) {
         int per_cu = 0;
-        const pa::DecodeKernels k = pa::decode_kernels(dt, s->head_dim, G, hpg);
+        const pa::DecodeKernels k = pa::decode_kernels(dt, s->head_dim, G, hpg, h8);
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k.main, k.threads, 0) !=
                 hipSuccess ||
             per_cu <= 0)
@@ -81,13 +102,6 @@ int decode_grid(const pa_shape *s)
     }
     return slot;
 }
-
-// Tokens per block (0 in the shape means 16) and the kernels' view of it:
-// every kernel walks 16-token units, block b holding units b * 2^s .. + 2^s - 1.
-int block_size_of(const pa_shape *s) { return s->block_size ? s->block_size : 16; }
-int unit_shift(const pa_shape *s) { return block_size_of(s) == 64 ? 2 : block_size_of(s) == 32 ? 1 : 0; }
-// 16-token units a block table row can address.
-int units_per_seq(const pa_shape *s) { return s->max_blocks_per_seq << unit_shift(s); }
 
 // Bytes of one block of one pool: block_size token rows of num_kv_heads x head_dim.
 int64_t block_bytes_of(const pa_shape *s)
@@ -130,10 +144,11 @@ pa_status check_shape(const pa_shape *s, bool need_tables)
                     s->num_kv_heads);
     if (s->num_blocks <= 0)
         return fail(PA_ERR_INVALID, "num_blocks must be positive");
-    if (s->block_size != 0 && s->block_size != 16 && s->block_size != 32 && s->block_size != 64)
-        return fail(PA_ERR_UNSUPPORTED, "block_size %d (16, 32 or 64 are built)", s->block_size);
-    if (s->num_blocks * (block_size_of(s) / 16) > (int64_t)1 << 31)
-        return fail(PA_ERR_UNSUPPORTED, "num_blocks * block_size / 16 above 2^31");
+    if (s->block_size != 0 && s->block_size != 8 && s->block_size != 16 && s->block_size != 32 &&
+        s->block_size != 64)
+        return fail(PA_ERR_UNSUPPORTED, "block_size %d (8, 16, 32 or 64 are built)", s->block_size);
+    if (kernel_blocks(s) > (int64_t)1 << 31)
+        return fail(PA_ERR_UNSUPPORTED, "num_blocks * max(block_size / 16, 1) above 2^31");
     if (need_tables && s->max_blocks_per_seq <= 0)
         return fail(PA_ERR_INVALID, "max_blocks_per_seq must be positive");
     if (s->cache_dtype != PA_F32 && s->cache_dtype != PA_BF16 && s->cache_dtype != PA_FP8_E4M3)
@@ -162,7 +177,7 @@ DecodeLayout decode_layout(const pa_shape *s)
     const int pb = s->partition_tokens > 0 ? s->partition_tokens / 16 : 0;
     DecodeLayout L;
     L.slots = pa::decode_partial_slots(s->num_seqs, s->num_kv_heads, G, units_per_seq(s), pb,
-                                       decode_grid(s));
+                                       decode_grid(s), unit_shift(s));
     L.count_bytes = (size_t)pa::kDecodeCounterSlots * sizeof(int32_t);
     L.ml_bytes = align256((size_t)L.slots * G * 2 * sizeof(float));
     L.acc_bytes = align256((size_t)L.slots * G * s->head_dim * sizeof(float));
@@ -337,7 +352,7 @@ pa_status pa_decode(float *out, const void *q, const void *k_cache, const void *
     a.head_dim = shape->head_dim;
     a.max_blocks = shape->max_blocks_per_seq;
     a.tbs_log2 = unit_shift(shape);
-    a.num_blocks = shape->num_blocks << a.tbs_log2;  // in 16-token units
+    a.num_blocks = kernel_blocks(shape);
     a.cache_dtype = shape->cache_dtype;
     a.part_blocks = shape->partition_tokens / 16;
     a.grid = decode_grid(shape);
@@ -414,7 +429,7 @@ pa_status pa_prefill_chunk(float *out, const void *q, const void *k_cache, const
     a.head_dim = shape->head_dim;
     a.max_blocks = shape->max_blocks_per_seq;
     a.tbs_log2 = unit_shift(shape);
-    a.num_blocks = shape->num_blocks << a.tbs_log2;  // in 16-token units
+    a.num_blocks = kernel_blocks(shape);
     a.cache_dtype = shape->cache_dtype;
     a.kv_splits = kv_splits;
     a.m_tiles = m_tiles;

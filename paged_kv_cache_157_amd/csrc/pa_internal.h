@@ -40,8 +40,9 @@ struct DecodeArgs {
     const int32_t *block_tables, *context_lens;
     int num_seqs, num_q_heads, num_kv_heads, head_dim;
     int max_blocks;        // width of a block table row (entries)
-    int tbs_log2;          // an entry names 2^tbs_log2 consecutive 16-token units
-    int64_t num_blocks;    // pool size in 16-token units
+    int tbs_log2;          // an entry names 2^tbs_log2 consecutive 16-token units; -1: an
+                           // entry names one 8-token block (a unit is two entries)
+    int64_t num_blocks;    // pool size in 16-token units (8-token blocks when tbs_log2 < 0)
     int cache_dtype;
     int part_blocks;       // 0: balanced split; else fixed partitions (16-token units)
     int grid;              // persistent work-group count
@@ -56,16 +57,18 @@ struct DecodeArgs {
 constexpr int64_t kDecodeCounterSlots = 1 << 20;
 // Number of partial-result records the decode workspace must hold.
 int64_t decode_partial_slots(int num_seqs, int num_kv_heads, int group, int max_blocks,
-                             int part_blocks, int grid);
+                             int part_blocks, int grid, int tbs_log2);
 bool decode_supported(int cache_dtype, int head_dim, int group);
 struct DecodeKernels {
     const void *main;    // persistent split-K decode kernel (merges its own partials)
     int threads;         // work-group size
 };
 // KV heads one decode work-group serves: 4 (the head-group kernel) when the
-// model has at least two groups of four KV heads and G >= 2, else 1.
-int decode_hpg(int num_kv_heads, int group);
-DecodeKernels decode_kernels(int cache_dtype, int head_dim, int group, int hpg);
+// model has at least two groups of four KV heads and G >= 2 and blocks hold 16
+// or more tokens (tbs_log2 >= 0), else 1.
+int decode_hpg(int num_kv_heads, int group, int tbs_log2);
+// h8: the one-KV-head kernel built for 8-token blocks
+DecodeKernels decode_kernels(int cache_dtype, int head_dim, int group, int hpg, bool h8);
 // the head-group kernels (decode_hg4.hip)
 DecodeKernels decode_hg4_kernels(int cache_dtype, int head_dim, int group);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
@@ -78,8 +81,9 @@ struct PrefillArgs {
     int64_t total_rows;
     int num_reqs, num_q_heads, num_kv_heads, head_dim;
     int max_blocks;        // width of a block table row (entries)
-    int tbs_log2;          // an entry names 2^tbs_log2 consecutive 16-token units
-    int64_t num_blocks;    // pool size in 16-token units
+    int tbs_log2;          // an entry names 2^tbs_log2 consecutive 16-token units; -1: an
+                           // entry names one 8-token block (a unit is two entries)
+    int64_t num_blocks;    // pool size in 16-token units (8-token blocks when tbs_log2 < 0)
     int cache_dtype;
     int kv_splits;
     int m_tiles;           // row tiles per (request, KV head), from the largest chunk

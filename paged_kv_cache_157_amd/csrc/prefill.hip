@@ -225,9 +225,15 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
         return;
     n = n < a.total_rows - qs ? n : (int)(a.total_rows - qs);
     int Ctx = a.context_lens[r];
-    const int ts = a.tbs_log2;  // a table entry names 2^ts consecutive 16-token units
-    const int maxU = a.max_blocks << ts;
-    Ctx = Ctx < 16 * maxU ? Ctx : 16 * maxU;  // caller precondition, enforced
+    // Rows are fetched in "parts" of PR = 2^hs consecutive rows held by one
+    // physical location: 16-token units (a table entry names 2^ts of them),
+    // or, with 8-token blocks (tbs_log2 < 0), single blocks.  Entry of part x:
+    // tab[x >> tsp] << tsp, plus x's place among the parts of that entry.
+    const bool h8 = a.tbs_log2 < 0;
+    const int hs = h8 ? 3 : 4, PR = 1 << hs;
+    const int tsp = h8 ? 0 : a.tbs_log2;
+    const int max_ctx = a.max_blocks * (PR << tsp);  // tokens a table row addresses
+    Ctx = Ctx < max_ctx ? Ctx : max_ctx;  // caller precondition, enforced
     const int P = Ctx - n;
     const int pos0 = mt * ppt;
     if (pos0 >= n)
@@ -280,7 +286,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
     // that reaches the products is finite.
     constexpr int SPR = C::SROWB / 16;  // 16-byte slots per cached row
     // per-lane byte offset of each of this wave's instructions inside its
-    // 16-token block (the same for every tile)
+    // part (the same for every tile)
     uint32_t doff[DPW];
 #pragma unroll
     for (int j = 0; j < DPW; ++j) {
@@ -289,24 +295,29 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
         const int ii = isv ? i - C::DMA_TILE / 2 : i;
         const int row = ii * C::DMA_ROWS + lane / SPR, slot = lane % SPR;
         const int ch = C::RAW ? slot : slot ^ (isv ? swz_v<D>(row) : swz_k<D>(row));
-        doff[j] = (uint32_t)((row & 15) * tok_bytes + ch * 16);
+        doff[j] = (uint32_t)((row & (PR - 1)) * tok_bytes + ch * 16);
     }
-    // 16-token units holding context (>= 1 whenever a tile is issued)
-    const int ctx_units = (Ctx + 15) >> 4;
-    // physical block entry of 16-token unit kb of tile kt (units past the
-    // context take the last one's entry; no row of theirs is fetched)
+    const int64_t part_bytes = (int64_t)PR * tok_bytes;
+    const int ppt_k = KT >> hs;  // parts per tile
+    // parts holding context (>= 1 whenever a tile is issued)
+    const int ctx_units = (Ctx + PR - 1) >> hs;
+    // physical part of part kb of tile kt (parts past the context take the
+    // last one's entry; no row of theirs is fetched)
     auto unit_entry = [&](int kt, int kb) -> int {
-        int blk = kt * (KT / 16) + kb;
+        int blk = kt * ppt_k + kb;
         blk = blk < ctx_units ? blk : ctx_units - 1;
-        const int e = (tab[blk >> ts] << ts) + (blk & ((1 << ts) - 1));
+        const int e = (tab[blk >> tsp] << tsp) + (blk & ((1 << tsp) - 1));
         return (unsigned)e < (unsigned)a.num_blocks ? e : 0;
     };
-    // Instruction j of this wave always moves rows of the same unit of a tile
-    // (DMA_ROWS divides 16).  With two or more instructions per wave, K
-    // instruction j and V instruction j + DPW / 2 move the same rows, so a wave
-    // needs the entries of DPW / 2 units; with one, of one unit.  The table
-    // entries are read here and used by issue_tile, so their loads go out back
-    // to back and are waited for only where the entries are needed.
+    // An instruction lies in one part when DMA_ROWS <= PR (not for 16-row fp8
+    // instructions over 8-token blocks: those always take the per-lane path).
+    // Instruction j of this wave then always moves rows of the same part of a
+    // tile.  With two or more instructions per wave, K instruction j and V
+    // instruction j + DPW / 2 move the same rows, so a wave needs the entries
+    // of DPW / 2 parts; with one, of one part.  The table entries are read here
+    // and used by issue_tile, so their loads go out back to back and are waited
+    // for only where the entries are needed.
+    const bool one_part = C::DMA_ROWS <= PR;
     static_assert((DPW == 1 || DPW % 2 == 0) && C::DMA_TILE == C::WAVES * DPW, "DMA layout");
     constexpr int NU = DPW >= 2 ? DPW / 2 : 1;
     struct Units {
@@ -317,17 +328,17 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
         for (int j = 0; j < NU; ++j) {
             const int i = w + C::WAVES * j;
             const int ii = DPW >= 2 || i < C::DMA_TILE / 2 ? i : i - C::DMA_TILE / 2;
-            int blk = kt * (KT / 16) + ((ii * C::DMA_ROWS) >> 4);
+            int blk = kt * ppt_k + ((ii * C::DMA_ROWS) >> hs);
             blk = blk < ctx_units ? blk : ctx_units - 1;
             un.blk[j] = blk;
-            un.raw[j] = tab[blk >> ts];
+            un.raw[j] = tab[blk >> tsp];
         }
     };
     auto issue_tile = [&](int kt, int s, const Units &un) {
         int pb[NU];
 #pragma unroll
         for (int j = 0; j < NU; ++j) {
-            const int e = (un.raw[j] << ts) + (un.blk[j] & ((1 << ts) - 1));
+            const int e = (un.raw[j] << tsp) + (un.blk[j] & ((1 << tsp) - 1));
             pb[j] = (unsigned)e < (unsigned)a.num_blocks ? e : 0;
         }
         const int last = Ctx - 1 - kt * KT;  // last context row of this tile (may exceed KT)
@@ -340,19 +351,26 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
                 uniform(lds_addr(sm.ring + s * C::STAGEB + (isv ? KT * C::SROWB : 0) + ii * 1024));
             const char *base = isv ? vbase : kbase;
             const int row0 = ii * C::DMA_ROWS;
-            if (row0 + C::DMA_ROWS - 1 <= last) {
-                // whole instruction inside the context: one block, scalar base
-                dma16(base + (int64_t)pb[j % NU] * 16 * tok_bytes + doff[j], dst);
+            if (one_part && row0 + C::DMA_ROWS - 1 <= last) {
+                // whole instruction inside the context and one part: scalar base
+                dma16(base + (int64_t)pb[j % NU] * part_bytes + doff[j], dst);
             } else {
-                // the context ends inside this instruction (last tile only)
-                const int p0 = unit_entry(kt, 0), p1 = unit_entry(kt, 1);
-                const int p2 = unit_entry(kt, 2), p3 = unit_entry(kt, 3);
+                // the context ends inside this instruction (last tile only), or
+                // the instruction spans two parts: each lane takes its row's part
+                int pe[8];
+#pragma unroll
+                for (int k = 0; k < 8; ++k)
+                    pe[k] = k < ppt_k ? unit_entry(kt, k) : 0;
                 const int row = row0 + lane / SPR, slot = lane % SPR;
                 const int key = row < last ? row : last;
-                const int kb = key >> 4;
-                const int p = kb == 0 ? p0 : kb == 1 ? p1 : kb == 2 ? p2 : p3;
+                const int kb = key >> hs;
+                int p = pe[0];
+#pragma unroll
+                for (int k = 1; k < 8; ++k)
+                    p = kb == k ? pe[k] : p;
                 const int ch = C::RAW ? slot : slot ^ (isv ? swz_v<D>(row) : swz_k<D>(row));
-                dma16(base + ((int64_t)p * 16 + (key & 15)) * tok_bytes + ch * 16, dst);
+                dma16(base + (int64_t)p * part_bytes + (int64_t)(key & (PR - 1)) * tok_bytes + ch * 16,
+                      dst);
             }
         }
     };

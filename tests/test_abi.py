@@ -65,7 +65,7 @@ def decode(shape, ws=FAKE, ws_bytes=1 << 40, ptr=FAKE, scale=0.1):
     (dict(cache_dtype=0, q_dtype=0, head_dim=128), binding.PA_ERR_UNSUPPORTED),
     (dict(q_dtype=0), binding.PA_ERR_UNSUPPORTED),
     (dict(partition_tokens=24), binding.PA_ERR_INVALID),
-    (dict(block_size=8), binding.PA_ERR_UNSUPPORTED),
+    (dict(block_size=4), binding.PA_ERR_UNSUPPORTED),
     (dict(block_size=48), binding.PA_ERR_UNSUPPORTED),
 ])
 def test_decode_rejects_bad_shapes(kw, status):

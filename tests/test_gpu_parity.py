@@ -300,11 +300,12 @@ def test_partitions_of_many_short_sequences():
 
 
 # ----------------------------------------------------------------------------
-# blocks of 32 and 64 tokens: every kernel walks 16-token units, a table
-# entry naming block_size / 16 consecutive ones
+# blocks of 8, 32 and 64 tokens: every kernel walks 16-token units, a table
+# entry naming block_size / 16 consecutive ones (32, 64) or half of one (8:
+# a unit's two halves in unrelated blocks; table widths odd and even)
 # ----------------------------------------------------------------------------
 
-BIG_BLOCKS = [(bs, storage, hkv, G, ptok) for bs in (32, 64)
+BIG_BLOCKS = [(bs, storage, hkv, G, ptok) for bs in (8, 32, 64)
               for storage, hkv, G, ptok in (("bf16", 2, 7, 0), ("bf16", 8, 4, 0), ("fp8", 8, 4, 512),
                                             ("fp8", 4, 1, 64), ("f32", 2, 3, 0))]
 
@@ -322,17 +323,18 @@ def test_decode_with_larger_blocks(bs, storage, hkv, G, ptok):
     assert max_err(got, oracle_problem(p)) <= TOL[storage]
 
 
-@pytest.mark.parametrize("bs", [32, 64])
+@pytest.mark.parametrize("bs,d", [(8, 128), (8, 64), (32, 128), (64, 128)])
 @pytest.mark.parametrize("storage", ["bf16", "fp8"])
-def test_prefill_with_larger_blocks(bs, storage):
-    hc = [(0, 77), (500, 100), (bs, 1)]
+def test_prefill_with_larger_blocks(bs, d, storage):
+    hc = [(0, 77), (500, 100), (bs, 1), (3 * bs + 3, 40)]
     lens = [h + n for h, n in hc]
-    p = random_problem(3100 + bs, len(hc), 32, 8, 128, lens,
+    say(f"prefill block_size={bs} d={d} {storage}")
+    p = random_problem(3100 + bs + d, len(hc), 32, 8, d, lens,
                        sum(-(-L // bs) for L in lens) + 3, storage, block_size=bs)
     qs = np.concatenate([[0], np.cumsum([n for _, n in hc])]).astype(np.int32)
     g = torch.Generator(device="cuda")
     g.manual_seed(3200 + bs)
-    qp = torch.randn((int(qs[-1]), 32, 128), generator=g, device="cuda").to(torch.bfloat16)
+    qp = torch.randn((int(qs[-1]), 32, d), generator=g, device="cuda").to(torch.bfloat16)
     out = torch.full(qp.shape, float("nan"), dtype=torch.float32, device="cuda")
     binding.prefill_chunk(out, qp, p["k"], p["v"], p["bt"], to_dev(qs), p["lens"], p["scale"],
                           kv_scale=p["kv_scale"])
@@ -342,7 +344,7 @@ def test_prefill_with_larger_blocks(bs, storage):
     assert max_err(out.cpu().numpy(), ref) <= TOL[storage]
 
 
-@pytest.mark.parametrize("bs", [32, 64])
+@pytest.mark.parametrize("bs", [8, 32, 64])
 def test_cache_write_and_copies_with_larger_blocks(bs):
     nblk, hkv, d = 50, 4, 128
     g = torch.Generator(device="cuda")

@@ -464,6 +464,34 @@ def test_larger_blocks_address_the_same_slots(B):
         np.testing.assert_allclose(out[0, 0], np.full(64, 1.0 / 38), rtol=0, atol=1e-15)
 
 
+def test_eight_token_blocks_address_the_same_slots():
+    """[L33] §2.2 with 8 tokens per block: a pool of 16-token blocks seen as
+    8-token blocks, every 16-block entry p becoming entries 2p and 2p + 1,
+    holds every token at the same slot, so both views give the same bits;
+    and token 13 of a sequence sits in its second block at offset 5."""
+    rng = np.random.default_rng(16)
+    lens = [1, 7, 8, 9, 16, 17, 83]
+    c = random_case(rng, len(lens), 8, 2, 64, lens, 40, "bf16")  # 16-slot view
+    nb16 = [-(-L // 16) for L in lens]
+    bt8 = np.full((len(lens), 2 * max(nb16)), -1, np.int32)
+    for i, n in enumerate(nb16):
+        for j in range(n):
+            bt8[i, 2 * j], bt8[i, 2 * j + 1] = 2 * c["bt"][i, j], 2 * c["bt"][i, j] + 1
+    # entries past a sequence's last 8-token block are never read
+    for i, L in enumerate(lens):
+        bt8[i, -(-L // 8):] = 10 ** 6
+    a = oracle.decode(c["q"], c["kpool"], c["vpool"], bt8, c["lens"], 0.125, block_size=8)
+    b = oracle.decode(c["q"], c["kpool"], c["vpool"], c["bt"], c["lens"], 0.125)
+    assert np.array_equal(a, b)
+    q = np.zeros((1, 1, 64), np.float32)
+    k1 = np.zeros((40 * 8, 1, 64), np.float32)
+    v1 = np.zeros_like(k1)
+    v1[9 * 8 + 5, 0] = 1.0
+    out = oracle.decode(q, k1, v1, np.array([[3, 9]], np.int32), np.array([14], np.int32), 1.0,
+                        block_size=8)
+    np.testing.assert_allclose(out[0, 0], np.full(64, 1.0 / 14), rtol=0, atol=1e-15)
+
+
 def test_unused_table_entries_are_never_read():
     rng = np.random.default_rng(8)
     c = random_case(rng, 2, 4, 2, 64, [17, 40], 8, "bf16")
