@@ -75,6 +75,9 @@ int64_t kernel_blocks(const pa_shape *s)
     return unit_shift(s) < 0 ? s->num_blocks : s->num_blocks << unit_shift(s);
 }
 
+// Work-groups per resident slot of the decode grid with fixed partitions.
+constexpr int kPartitionGridFactor = 3;
+
 // Persistent decode grid: as many work-groups as can be resident at once
 // (compute units x occupancy of the kernel that serves this shape), so every
 // work-group of the balanced split runs concurrently.
@@ -355,7 +358,12 @@ pa_status pa_decode(float *out, const void *q, const void *k_cache, const void *
     a.num_blocks = kernel_blocks(shape);
     a.cache_dtype = shape->cache_dtype;
     a.part_blocks = shape->partition_tokens / 16;
-    a.grid = decode_grid(shape);
+    // Fixed partitions are whole work items, so static ranges of them cannot
+    // balance; three times the resident work-groups lets the dispatcher hand
+    // the later ones to the CUs that finish first (measured: 2x and 4-8x are
+    // slower on the 32k/short skewed batch; the balanced split balances by
+    // itself and loses with any oversubscription).
+    a.grid = decode_grid(shape) * (shape->partition_tokens > 0 ? kPartitionGridFactor : 1);
     const float kvs = kv_scale_of(shape);
     a.qk_scale = scale * 1.4426950408889634f * kvs;
     a.v_scale = kvs;
