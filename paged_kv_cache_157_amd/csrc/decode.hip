@@ -440,9 +440,8 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(DecodeArgs a)
         }
         const unsigned b0 = (unsigned)p.a < nblocks_pool ? (unsigned)p.a : 0u;
         const unsigned b1 = (unsigned)p.b < nblocks_pool ? (unsigned)p.b : 0u;
-        const char *lo = hbase + (int64_t)b0 * half_bytes;
-        const char *hi = hbase + (int64_t)b1 * half_bytes - half_bytes;
-        return (off >= (unsigned)half_bytes ? hi : lo) + off;
+        const bool upper = off >= (unsigned)half_bytes;
+        return hbase + (int64_t)(upper ? b1 : b0) * half_bytes + (upper ? off - (unsigned)half_bytes : off);
     };
 
     // per-lane byte offsets of the K and V chunks this lane fetches inside one
