@@ -356,18 +356,20 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
                 dma16(base + (int64_t)pb[j % NU] * part_bytes + doff[j], dst);
             } else {
                 // the context ends inside this instruction (last tile only), or
-                // the instruction spans two parts: each lane takes its row's part
-                int pe[8];
-#pragma unroll
-                for (int k = 0; k < 8; ++k)
-                    pe[k] = k < ppt_k ? unit_entry(kt, k) : 0;
+                // the instruction spans two parts: each lane takes its row's
+                // part, one of the (at most) two the aligned rows fall in
+                // (DMA_ROWS <= 16, parts of 8 or 16 rows).  Rows past the
+                // context read the last context row: in one of those two parts,
+                // or, when the whole instruction is past the context, in an
+                // earlier part whose entry both candidates then hold (a part past
+                // the context takes the last context part's entry).
+                static_assert(C::DMA_ROWS <= 16, "an instruction spans at most two parts");
+                const int kb0 = row0 >> hs;
+                const int pa0 = unit_entry(kt, kb0);
+                const int pa1 = kb0 + 1 < ppt_k ? unit_entry(kt, kb0 + 1) : pa0;
                 const int row = row0 + lane / SPR, slot = lane % SPR;
                 const int key = row < last ? row : last;
-                const int kb = key >> hs;
-                int p = pe[0];
-#pragma unroll
-                for (int k = 1; k < 8; ++k)
-                    p = kb == k ? pe[k] : p;
+                const int p = (key >> hs) == kb0 ? pa0 : pa1;
                 const int ch = C::RAW ? slot : slot ^ (isv ? swz_v<D>(row) : swz_k<D>(row));
                 dma16(base + (int64_t)p * part_bytes + (int64_t)(key & (PR - 1)) * tok_bytes + ch * 16,
                       dst);
