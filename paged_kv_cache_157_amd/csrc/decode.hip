@@ -298,16 +298,30 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(DecodeArgs a)
             virt = (long long)(n > 0 ? n + ALPHA : 0) * Hkv;
         };
         long long tot = 0, totv = 0;
-        for (int base = 0; base < S; base += 64) {
-            const int s2 = base + lane;
-            long long r, v;
-            counts(s2 < S ? a.context_lens[s2] : 0, r, v);
-            if (narrow) {
-                tot += __builtin_amdgcn_readlane(wave_scan32((int)r), 63);
-                totv += __builtin_amdgcn_readlane(wave_scan32((int)v), 63);
-            } else {
-                tot += wave_sum64(r);
-                totv += wave_sum64(v);
+        // up to 64 sequences with narrow counts: one load of the lengths and
+        // one pair of prefix sums serve the totals and the search below
+        const bool one_pass = narrow && S <= 64;
+        int l0 = 0, ri0 = 0, vi0 = 0;
+        long long rr0 = 0, vv0 = 0;
+        if (one_pass) {
+            l0 = lane < S ? a.context_lens[lane] : 0;
+            counts(l0, rr0, vv0);
+            ri0 = wave_scan32((int)rr0);
+            vi0 = wave_scan32((int)vv0);
+            tot = __builtin_amdgcn_readlane(ri0, 63);
+            totv = __builtin_amdgcn_readlane(vi0, 63);
+        } else {
+            for (int base = 0; base < S; base += 64) {
+                const int s2 = base + lane;
+                long long r, v;
+                counts(s2 < S ? a.context_lens[s2] : 0, r, v);
+                if (narrow) {
+                    tot += __builtin_amdgcn_readlane(wave_scan32((int)r), 63);
+                    totv += __builtin_amdgcn_readlane(wave_scan32((int)v), 63);
+                } else {
+                    tot += wave_sum64(r);
+                    totv += wave_sum64(v);
+                }
             }
         }
         const bool virt = PB == 0 && ALPHA > 0 && totv >= (long long)(ALPHA + 2) * W;
@@ -352,14 +366,18 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(DecodeArgs a)
         int seq0, seq1;
         long long rb0, vb0, rb1, vb1;
         long long r0, r1;
-        if (narrow && S <= 64) {
-            // one pass: both prefix sums once, totals and the found lane read
-            // with scalar lane reads
-            const int l = lane < S ? a.context_lens[lane] : 0;
-            long long rr, vv;
-            counts(l, rr, vv);
-            const int ri = wave_scan32((int)rr), vi = wave_scan32((int)vv);
+        if (one_pass) {
+            // the prefix sums above, the found lane read with scalar lane
+            // reads; 32-bit divisions wherever the operands fit (T * W < 2^31:
+            // every position, count and quotient below is under T)
+            const int l = l0;
+            const long long rr = rr0, vv = vv0;
+            const int ri = ri0, vi = vi0;
             const int n = items_of(l);
+            const bool d32 = T * W < (1ll << 31);
+            auto div = [&](long long num, long long den) -> long long {
+                return d32 ? (long long)((unsigned)num / (unsigned)den) : num / den;
+            };
             auto find = [&](long long x, int &seq, long long &rbase, long long &vbase) -> long long {
                 seq = -1;
                 rbase = tot;
@@ -376,11 +394,11 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(DecodeArgs a)
                     return x;
                 const int nn = __builtin_amdgcn_readlane(n, l2);
                 const long long rel = x - vbase;
-                const long long gq = rel / (nn + ALPHA), xv = rel - gq * (nn + ALPHA);
+                const long long gq = div(rel, nn + ALPHA), xv = rel - gq * (nn + ALPHA);
                 return rbase + gq * nn + (xv > ALPHA ? xv - ALPHA : 0);
             };
-            r0 = find(T * blockIdx.x / W, seq0, rb0, vb0);
-            r1 = find(T * (blockIdx.x + 1) / W, seq1, rb1, vb1);
+            r0 = find(div(T * blockIdx.x, W), seq0, rb0, vb0);
+            r1 = find(div(T * (blockIdx.x + 1), W), seq1, rb1, vb1);
         } else {
             r0 = locate(T * blockIdx.x / W, seq0, rb0, vb0);
             r1 = locate(T * (blockIdx.x + 1) / W, seq1, rb1, vb1);
