@@ -37,6 +37,13 @@
  *     are distinct.  Kernels skip cache writes whose slot is out of range.
  *   - The library allocates no device memory.  Scratch space is passed in as
  *     `workspace`, sized by the matching *_workspace_bytes() call.
+ *   - Process-wide state: none that a call's data passes through.  The
+ *     library memoises two device properties per device id (its compute-unit
+ *     count, and how many work-groups of each decode kernel fit on a compute
+ *     unit), in write-once tables guarded by a mutex; the decode grid, the
+ *     prefill key split and the workspace sizes are derived from them, so
+ *     they depend on the device the call runs on.  Every entry point may be
+ *     called from several host threads at once.
  */
 #ifndef PA_H
 #define PA_H
@@ -161,7 +168,14 @@ size_t pa_decode_workspace_bytes(const pa_shape *shape);
  *                  results.  The counter region must be zero before the first
  *                  call that uses the buffer; every call leaves it zero again,
  *                  so a buffer zeroed once can be reused by calls of any shape.
- *                  Calls that run concurrently need separate workspaces.
+ *                  Calls that may run at the same time (on different streams)
+ *                  need separate workspaces: they would race on the counters
+ *                  and partial results.  Calls queued on one stream may share
+ *                  one.  A call that returns an error has launched nothing and
+ *                  left the counters as they were; only a kernel aborted in
+ *                  flight (a device fault, which ends the HIP context) can
+ *                  leave them nonzero, so a workspace from before such a fault
+ *                  must be zeroed again before reuse.
  *   A call is one kernel launch: partial results of a sequence split across
  *   work-groups are merged by the work-group that finishes last.
  *   Requires num_seqs * num_kv_heads <= 2^20.
@@ -171,7 +185,9 @@ pa_status pa_decode(float *out, const void *q, const void *k_cache, const void *
                     const pa_shape *shape, void *workspace, size_t workspace_bytes,
                     void *stream);
 
-/* Workspace bytes pa_prefill_chunk needs for total_query_rows rows. */
+/* Workspace bytes pa_prefill_chunk needs for total_query_rows rows (depends
+ * on the shape, the row count and the device's compute-unit count, which
+ * sets how many key-range splits the call uses). */
 size_t pa_prefill_workspace_bytes(const pa_shape *shape, int64_t total_query_rows);
 
 /*

@@ -120,22 +120,38 @@ def make_shape(q_heads: int, k_cache: torch.Tensor, q_dtype: torch.dtype, num_se
                    partition_tokens=int(partition_tokens), block_size=k_cache.shape[1])
 
 
-_workspaces: Dict[Tuple[int, str], torch.Tensor] = {}
+_workspaces: Dict[Tuple[int, int, str], torch.Tensor] = {}
 
 
 def _workspace(device: torch.device, nbytes: int, op: str) -> Optional[torch.Tensor]:
-    """Scratch buffer of one entry point, reused across its calls on a device
-    (grown when needed; calls on one stream are ordered, so reuse is safe)."""
+    """Scratch buffer of one entry point, reused across its calls on one
+    stream of a device.
+
+    Calls on one stream run in order, so they can share a buffer; calls on
+    different streams may run at the same time and would race on the decode's
+    arrival counters and partial results, so every stream gets its own
+    buffer.  The buffer is allocated (zero-filled: pa_decode's arrival
+    counters must start at zero, and every call leaves them zero again) while
+    that stream is current, so the caching allocator ties it to that stream;
+    a buffer replaced by a larger one is released in that stream's order, after
+    the calls already queued on it."""
     if nbytes == 0:
         return None
-    key = (device.index if device.index is not None else torch.cuda.current_device(), op)
+    dev = device.index if device.index is not None else torch.cuda.current_device()
+    key = (dev, torch.cuda.current_stream(device).cuda_stream, op)
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
-        # zero-filled once: pa_decode's arrival counters must start at zero (every
-        # call leaves them zero again); nothing else in it needs initialisation
         ws = torch.zeros(nbytes, dtype=torch.uint8, device=device)
         _workspaces[key] = ws
     return ws
+
+
+def workspace_of(op: str, device: Optional[torch.device] = None) -> Optional[torch.Tensor]:
+    """The buffer the current stream of `device` uses for `op` ("decode" or
+    "prefill"), or None before its first call."""
+    device = device or torch.device("cuda", torch.cuda.current_device())
+    dev = device.index if device.index is not None else torch.cuda.current_device()
+    return _workspaces.get((dev, torch.cuda.current_stream(device).cuda_stream, op))
 
 
 def reshape_and_cache(k: torch.Tensor, v: torch.Tensor, k_cache: torch.Tensor,
@@ -216,7 +232,12 @@ def decode(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor, v_cache: t
            block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
            partition_tokens: int = 0, kv_scale: float = 1.0,
            workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """pa_decode: out[S, Hq, d] (fp32) = paged single-query attention."""
+    """pa_decode: out[S, Hq, d] (fp32) = paged single-query attention.
+
+    Runs on the current stream of the pools' device.  Without `workspace`,
+    the stream's own cached buffer is used (one per stream, see _workspace);
+    a caller-provided workspace must not be shared by calls that may run at
+    the same time (different streams)."""
     dev = k_cache.device
     _require(out, "out", dev, torch.float32, 3)
     _require(q, "q", dev, None, 3)
@@ -250,7 +271,10 @@ def prefill_chunk(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor,
                   v_cache: torch.Tensor, block_tables: torch.Tensor, query_start: torch.Tensor,
                   context_lens: torch.Tensor, scale: float, kv_scale: float = 1.0,
                   workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """pa_prefill_chunk: out[Tq, Hq, d] (fp32) for chunks over their paged history."""
+    """pa_prefill_chunk: out[Tq, Hq, d] (fp32) for chunks over their paged history.
+
+    Runs on the current stream of the pools' device; the workspace rules are
+    those of decode()."""
     dev = k_cache.device
     _require(out, "out", dev, torch.float32, 3)
     _require(q, "q", dev, torch.bfloat16, 3)

@@ -36,7 +36,10 @@ pa_status hip_fail(hipError_t e, const char *what)
     return fail(PA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-// Compute units of the current device (cached per device id).
+// Compute units of the current device.  Device properties (this count and
+// the decode kernels' occupancy below) are memoised per device id in
+// write-once tables under a mutex: they never change while the process runs,
+// and no call's data passes through them.
 int device_cus()
 {
     static std::mutex mu;
@@ -379,7 +382,7 @@ size_t pa_prefill_workspace_bytes(const pa_shape *shape, int64_t total_query_row
 {
     if (check_shape(shape, true) != PA_OK || total_query_rows < 0)
         return 0;
-    const int ks = pa::prefill_kv_splits(total_query_rows, shape->num_q_heads);
+    const int ks = pa::prefill_kv_splits(total_query_rows, shape->num_q_heads, device_cus());
     if (ks <= 1)
         return 0;
     const size_t rows = (size_t)total_query_rows * shape->num_q_heads;
@@ -413,7 +416,7 @@ pa_status pa_prefill_chunk(float *out, const void *q, const void *k_cache, const
     if (shape->num_seqs == 0 || total_query_rows == 0)
         return ok();
     const int m_tiles = pa::prefill_m_tiles(total_query_rows, shape->num_q_heads, shape->num_kv_heads);
-    const int kv_splits = pa::prefill_kv_splits(total_query_rows, shape->num_q_heads);
+    const int kv_splits = pa::prefill_kv_splits(total_query_rows, shape->num_q_heads, device_cus());
     if ((int64_t)m_tiles * shape->num_kv_heads * kv_splits > INT32_MAX)
         return fail(PA_ERR_UNSUPPORTED, "prefill grid too large");
     if (!out || !q || !k_cache || !v_cache || !block_tables || !query_start || !context_lens)

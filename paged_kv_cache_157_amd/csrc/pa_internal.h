@@ -92,7 +92,9 @@ struct PrefillArgs {
     float *ws_ml;          // [kv_splits][rows*Hq][2]
 };
 bool prefill_supported(int cache_dtype, int head_dim, int group);
-int prefill_kv_splits(int64_t total_rows, int num_q_heads);
+// Key-range splits of a prefill call: enough (row tile, KV head, split)
+// work-groups to give each of the device's `cus` compute units one, at most 16.
+int prefill_kv_splits(int64_t total_rows, int num_q_heads, int cus);
 int prefill_m_tiles(int64_t total_rows, int num_q_heads, int num_kv_heads);
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);
 

@@ -191,12 +191,12 @@ __device__ __forceinline__ void wait_tiles_in_flight(int n)
 // Issued as inline assembly so that the compiler, which would otherwise wait
 // for these loads before every transposing LDS read, leaves the counting to
 // wait_vm; the LDS reads then schedule freely between the matrix products.
+// The LDS address is an input bound to m0 ("{m0}"), so the compiler writes
+// that register itself and knows it is read here; the s_nop separates that
+// write from the load that reads it.
 __device__ __forceinline__ void dma16(const void *src, uint32_t lds_dst)
 {
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-                 :
-                 : "v"(src), "s"(lds_dst)
-                 : "memory", "m0");
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "{m0}"(lds_dst) : "memory");
 }
 
 template <int CDT, int D>
@@ -694,13 +694,13 @@ int prefill_m_tiles(int64_t total_rows, int num_q_heads, int num_kv_heads)
     return (int)((total_rows + ppt - 1) / ppt);
 }
 
-int prefill_kv_splits(int64_t total_rows, int num_q_heads)
+int prefill_kv_splits(int64_t total_rows, int num_q_heads, int cus)
 {
-    // one work-group per CU of a 256-CU device: split the key range until the
-    // (row tile, KV head) work-groups reach that count
+    // one work-group per compute unit: split the key range until the
+    // (row tile, KV head) work-groups reach the device's CU count
     const int64_t tiles = (total_rows * num_q_heads + PrefillCfg<DT_BF16, 128>::MROWS - 1) /
                           PrefillCfg<DT_BF16, 128>::MROWS;
-    int64_t ks = tiles > 0 ? 256 / tiles : 1;
+    int64_t ks = tiles > 0 ? cus / tiles : 1;
     if (ks < 1)
         ks = 1;
     if (ks > 16)

@@ -128,16 +128,6 @@ class StepRun:
         return err
 
 
-def sample_pairs(S: int, H: int, n: int, lens: np.ndarray, seed: int = 0):
-    """(seq, head) sample: the longest and shortest sequences plus random ones."""
-    rng = np.random.default_rng(seed)
-    seqs = list(rng.integers(0, S, size=n))
-    seqs += [int(np.argmax(lens)), int(np.argmin(lens))]
-    heads = list(rng.integers(0, H, size=len(seqs)))
-    heads[-2:] = [H - 1, 0]
-    return np.array(seqs, np.int32), np.array(heads, np.int32)
-
-
 def to_dev(a: np.ndarray, dtype=None) -> torch.Tensor:
     t = torch.from_numpy(np.ascontiguousarray(a))
     return t.to("cuda") if dtype is None else t.to("cuda").view(dtype)
