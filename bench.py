@@ -7,18 +7,30 @@ new tokens (pa_reshape_and_cache), the decode attention of every sequence
 (pa_prefill_chunk).  Inputs are seeded synthetic tensors already resident in
 HBM before the timed region.
 
-    python bench.py [--steps K] [--warmup W] [--workload qwen7b] [--no-cpu-baseline] [--extras]
+    python bench.py [--steps K] [--warmup W] [--workload qwen7b] [--no-cpu-baseline]
+                    [--no-configs] [--extras]
     python bench.py --workload replay_qwen7b
 
-Prints one JSON line.  `value` is the effective KV bandwidth of the step: KV
-bytes the decode must read (each sequence's K and V rows, once) divided by
-the step time.  The roofline entry is for the decode launch (one kernel),
-timed with HIP events on the stream the kernel runs on, in a second pass
-right after the timed steps.  The cache write, shorter than one host
-submission, is timed over 200 launches queued behind a GPU-side wait.
-``--extras`` adds the decode with the Infinity Cache evicted, a plain device
-copy, and the block copy and swap kernels.  A replay_* workload runs the
-continuous-batching replay instead and reports its steady state.
+Prints one JSON line.  `value` is the effective KV bandwidth of the headline
+step (the Qwen2.5-7B-shaped decode batch by default): KV bytes the decode
+must read (each sequence's K and V rows, once) divided by the step time.
+
+The roofline entry is for the decode launch (one kernel):
+  * `achieved` / `frac`: warm, i.e. max(K, 200) back-to-back launches timed
+    with one pair of HIP events on the stream the kernel runs on, right after
+    the timed steps (part of a 310 MB batch then comes from the 256 MB
+    Infinity Cache);
+  * `cold`: the same launch with the Infinity Cache evicted before every
+    launch (a 768 MiB read in between, subtracted), median and minimum, which
+    is what a model's layer sees when it reads its KV once per step.
+The cache write, shorter than one host submission, is timed over launches
+queued behind a GPU-side wait.  Unless --no-configs is given, the other
+workloads (13B MHA with a shared prefix, the skewed long/short mix, and the
+chunked-prefill mixed step with bf16 and fp8 caches) follow, each with the
+same W warm-up and K timed steps, and go into `configs`.
+``--extras`` adds a plain device copy, the block copy and swap kernels and
+the block-size sweep.  A replay_* workload runs the continuous-batching
+replay instead and reports its steady state.
 """
 from __future__ import annotations
 
@@ -39,6 +51,7 @@ HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 METRIC = "paged decode attention: effective KV HBM GB/s (% of peak) and tokens/s, 1 GPU"
 HOST_CORE_SHARE = 16
+TIMING_LAUNCHES = 200  # least number of back-to-back launches a kernel's time is taken over
 
 
 def parse():
@@ -49,11 +62,13 @@ def parse():
     ap.add_argument("--workload", default="qwen7b", choices=sorted(CONFIGS) + sorted(REPLAYS),
                     help="a one-step workload, or a continuous-batching replay (replay_*)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="measure the headline workload only (no sub-records for the others)")
+    ap.add_argument("--no-cold", action="store_true",
+                    help="skip the decode with the Infinity Cache evicted")
     ap.add_argument("--extras", action="store_true",
-                    help="also measure the decode with the Infinity Cache evicted, a plain "
-                         "device copy, pa_copy_blocks and pa_swap_blocks (after the timed "
-                         "steps; off by default so that a profile of the default command "
-                         "holds the warm decode launches only)")
+                    help="also measure a plain device copy, pa_copy_blocks, pa_swap_blocks and "
+                         "the block-size sweep (after the timed steps)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB "
                          "(a known-size reference for hardware byte counters)")
@@ -114,8 +129,19 @@ def partial_bytes(cfg, step) -> int:
     return int(parts[parts > 1].sum()) * cfg.num_kv_heads * G * (cfg.head_dim + 2) * 4 * 2
 
 
+def host_cpus() -> dict:
+    """The host's logical CPUs and the ones this process may run on."""
+    try:
+        allowed = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        allowed = os.cpu_count() or 1
+    return dict(host_logical_cpus=os.cpu_count() or 1, allowed_cpus=allowed)
+
+
 def cpu_baseline(cfg, step) -> dict:
-    """The CPU oracle, as it stands, on a bounded sample of the same batch."""
+    """The CPU oracle, as it stands, on a bounded sample of the same batch.
+    It runs with one thread per CPU this process may use, at most the box's
+    16-CPU share of the host (OMP_NUM_THREADS when set)."""
     import oracle  # test infrastructure: used only for this baseline leg
 
     def host_bits(t):
@@ -128,7 +154,9 @@ def cpu_baseline(cfg, step) -> dict:
     def pool_rows(a):
         return a.reshape(a.shape[0] * a.shape[1], a.shape[2], a.shape[3])
 
-    cores = min(HOST_CORE_SHARE, os.cpu_count() or 1)
+    cpus = host_cpus()
+    share = int(os.environ.get("OMP_NUM_THREADS", HOST_CORE_SHARE) or HOST_CORE_SHARE)
+    cores = max(1, min(share, cpus["allowed_cpus"]))
     kp = host_bits(step.k_cache)
     vp = host_bits(step.v_cache)
     q = host_bits(step.q)
@@ -157,25 +185,81 @@ def cpu_baseline(cfg, step) -> dict:
     passes = n_seq / cfg.num_seqs
     return dict(value=round(done_bytes / used / 1e9, 4), unit="GB/s", cores=cores, kind="oracle",
                 sample=f"{n_seq} sequence decodes ({passes:.2f} passes over the {cfg.num_seqs}-sequence "
-                       f"batch, longest first), all {cfg.num_q_heads} heads, {used:.1f} s")
+                       f"batch, longest first), all {cfg.num_q_heads} heads, {used:.1f} s",
+                **cpus)
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no "
-              "multi-GPU path", file=sys.stderr)
-        sys.exit(2)
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        sys.exit(2)
-    binding.load()
-    if args.workload in REPLAYS:
-        replay_main(args)
-        return
-    cfg = CONFIGS[args.workload]
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
+class Timer:
+    """GPU-side timing helpers on torch's current stream (the stream every
+    libpa call of this script is queued on)."""
+
+    def __init__(self):
+        self.e0 = torch.cuda.Event(enable_timing=True)
+        self.e1 = torch.cuda.Event(enable_timing=True)
+        # torch.cuda._sleep spins for a number of GPU clock ticks; ticks per
+        # millisecond are measured once here
+        probe_ticks = 1 << 22
+        torch.cuda._sleep(probe_ticks)
+        self.e0.record()
+        torch.cuda._sleep(probe_ticks)
+        self.e1.record()
+        torch.cuda.synchronize()
+        self.ticks_per_ms = probe_ticks / max(self.e0.elapsed_time(self.e1), 1e-3)
+
+    def launch_ms(self, fn, n, hold=False):
+        """Average duration of one launch of fn: HIP events recorded on the stream
+        the kernels run on (torch's current stream) around n back-to-back launches
+        (one event pair, so the event cost is spread over n launches).  With
+        `hold`, the launches are queued behind a GPU-side wait long enough for
+        the host to submit all of them, so that a kernel shorter than one host
+        submission (the cache write) is timed on the GPU and not at the host's
+        pace.  Longer kernels are timed without it: the GPU is then the
+        bottleneck anyway, and an idle wait lets its clocks drop."""
+        fn()
+        if hold:
+            torch.cuda._sleep(int(self.ticks_per_ms * (0.5 + 0.03 * n)))
+        self.e0.record()
+        for _ in range(n):
+            fn()
+        self.e1.record()
+        torch.cuda.synchronize()
+        return self.e0.elapsed_time(self.e1) / n
+
+    def cold_us(self, fn, evict, n=20, reps=5):
+        """Launch time of fn with its inputs evicted from the 256 MB Infinity
+        Cache: n rounds of (a read of `evict`, larger than that cache, then fn)
+        back to back, minus n reads alone, per round; median and minimum over
+        `reps` repetitions."""
+        ts = []
+        for _ in range(reps):
+            t = []
+            for with_fn in (True, False):
+                evict.sum()
+                torch.cuda.synchronize()
+                self.e0.record()
+                for _ in range(n):
+                    evict.sum()
+                    if with_fn:
+                        fn()
+                self.e1.record()
+                torch.cuda.synchronize()
+                t.append(self.e0.elapsed_time(self.e1))
+            ts.append((t[0] - t[1]) / n * 1e3)
+        return dict(median_us=round(float(np.median(ts)), 2), min_us=round(float(np.min(ts)), 2),
+                    launches=n * reps)
+
+
+def prefill_flops(cfg) -> int:
+    """4 d Hq flops (QK^T and PV) per (query row, attended key) of the chunk:
+    row j of the chunk attends history + j + 1 keys."""
+    return cfg.num_q_heads * cfg.head_dim * 4 * sum(
+        cfg.prefill_history + j + 1 for j in range(cfg.prefill_chunk))
+
+
+def measure(cfg, args, dev, timer: Timer, headline: bool) -> dict:
+    """One workload: W warm-up and K timed steps (cache write, [prefill,]
+    decode) back to back, then the per-launch times of its kernels."""
+    print(f"bench: {cfg.name}: inputs", file=sys.stderr, flush=True)
     step = make_step(cfg, dev)
     out = torch.empty(step.q.shape, dtype=torch.float32, device=dev)
     out_pre = None
@@ -218,63 +302,88 @@ def main():
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
 
-    # GPU-side wait: torch.cuda._sleep spins for a number of GPU clock ticks;
-    # ticks per millisecond are measured once here
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    probe_ticks = 1 << 22
-    torch.cuda._sleep(probe_ticks)
-    e0.record()
-    torch.cuda._sleep(probe_ticks)
-    e1.record()
-    torch.cuda.synchronize()
-    ticks_per_ms = probe_ticks / max(e0.elapsed_time(e1), 1e-3)
-
-    def launch_ms(fn, n, hold=False):
-        """Average duration of one launch of fn: HIP events recorded on the stream
-        the kernels run on (torch's current stream) around n back-to-back launches
-        (one event pair, so the event cost is spread over n launches).  With
-        `hold`, the launches are queued behind a GPU-side wait long enough for
-        the host to submit all of them, so that a kernel shorter than one host
-        submission (the cache write) is timed on the GPU and not at the host's
-        pace.  Longer kernels are timed without it: the GPU is then the
-        bottleneck anyway, and an idle wait lets its clocks drop."""
-        fn()
-        if hold:
-            torch.cuda._sleep(int(ticks_per_ms * (0.5 + 0.03 * n)))
-        e0.record()
-        for _ in range(n):
-            fn()
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / n
-
-    dec_ms = launch_ms(decode, args.steps)
-    pre_ms = launch_ms(prefill, args.steps) if out_pre is not None else None
+    print(f"bench: {cfg.name}: {args.steps} steps in {ms_per_step * args.steps:.1f} ms",
+          file=sys.stderr, flush=True)
+    # per-launch times: at least TIMING_LAUNCHES back-to-back launches, so that
+    # a short run (few timed steps) does not report its first, slow launches
+    n_time = max(args.steps, TIMING_LAUNCHES)
+    dec_ms = timer.launch_ms(decode, n_time)
+    pre_ms = timer.launch_ms(prefill, n_time) if out_pre is not None else None
     # held launches: at most 200 per event pair (HIP's queue depth)
-    cw_ms = launch_ms(cache_write, min(args.steps, 200), hold=True)
+    cw_ms = timer.launch_ms(cache_write, min(args.steps, 200), hold=True)
 
-    def cold_us(fn, evict, n=20, reps=5):
-        """Launch time of fn with its inputs evicted from the 256 MB Infinity
-        Cache: n rounds of (a read of `evict`, larger than that cache, then fn)
-        back to back, minus n reads alone, per round; median and minimum over
-        `reps` repetitions."""
-        ts = []
-        for _ in range(reps):
-            t = []
-            for with_fn in (True, False):
-                evict.sum()
-                torch.cuda.synchronize()
-                e0.record()
-                for _ in range(n):
-                    evict.sum()
-                    if with_fn:
-                        fn()
-                e1.record()
-                torch.cuda.synchronize()
-                t.append(e0.elapsed_time(e1))
-            ts.append((t[0] - t[1]) / n * 1e3)
-        return dict(median=round(float(np.median(ts)), 2), min=round(float(np.min(ts)), 2),
-                    rounds=n * reps)
+    ab = algorithmic_bytes(cfg, step)
+    uniq = unique_kv_bytes(cfg, step)
+    tokens_per_step = cfg.num_seqs + (cfg.prefill_chunk if out_pre is not None else 0)
+    kv_gbs = ab["kv"] / (ms_per_step * 1e-3) / 1e9
+    rec = dict(
+        workload=f"{cfg.name}: {cfg.title}",
+        num_seqs=cfg.num_seqs, q_heads=cfg.num_q_heads, kv_heads=cfg.num_kv_heads,
+        head_dim=cfg.head_dim, cache_dtype=cfg.cache_dtype, block_size=16,
+        pool_blocks=cfg.num_blocks, partition_tokens=cfg.partition_tokens,
+        context_tokens=int(step.plan.context_lens.sum()),
+        new_tokens=int(len(step.plan.slot_mapping)), seed=cfg.seed,
+        steps=args.steps, warmup=args.warmup,
+        ms_per_step=round(ms_per_step, 5),
+        step_kv_gbs=round(kv_gbs, 2),
+        tokens_per_step=tokens_per_step,
+        tokens_per_s=round(tokens_per_step / (ms_per_step * 1e-3), 1),
+        decode_kernel=decode_kernel_name(cfg),
+        decode_us=round(dec_ms * 1e3, 2),
+        decode_kv_bytes=ab["kv"],
+        decode_algorithmic_bytes=ab["total"],
+        decode_kv_gbs=round(ab["kv"] / (dec_ms * 1e-3) / 1e9, 2),
+        decode_achieved_gbs=round(ab["total"] / (dec_ms * 1e-3) / 1e9, 2),
+        decode_frac_of_hbm_peak=round(ab["total"] / (dec_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        cache_write_us=round(cw_ms * 1e3, 2),
+    )
+    if uniq < ab["kv"]:  # shared blocks: the distinct bytes read as well
+        rec["unique_kv_bytes"] = uniq
+        rec["decode_unique_kv_gbs"] = round(uniq / (dec_ms * 1e-3) / 1e9, 2)
+    if cfg.partition_tokens > 0:
+        rec["partial_bytes_per_launch"] = partial_bytes(cfg, step)
+    if pre_ms is not None:
+        fl = prefill_flops(cfg)
+        rec["prefill_us"] = round(pre_ms * 1e3, 2)
+        rec["prefill_gflop"] = round(fl / 1e9, 2)
+        rec["prefill_tflops"] = round(fl / (pre_ms * 1e-3) / 1e12, 2)
+        rec["prefill_pct_of_bf16_mfma_peak"] = round(
+            100.0 * rec["prefill_tflops"] / MFMA_BF16_PEAK_TFLOPS, 2)
+    if headline and not args.no_cold:
+        evict = torch.ones(192 << 20, dtype=torch.float32, device=dev)  # 768 MiB
+        cold = timer.cold_us(decode, evict)
+        del evict
+        cold["achieved_gbs"] = round(ab["total"] / (cold["median_us"] * 1e-6) / 1e9, 2)
+        cold["frac"] = round(cold["achieved_gbs"] / HBM_PEAK_GBS, 4)
+        rec["decode_cold"] = cold
+    if headline:
+        rec["_step"] = step
+        rec["_fns"] = dict(decode=decode, cache_write=cache_write, out=out)
+    return rec
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no "
+              "multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    binding.load()
+    if args.workload in REPLAYS:
+        replay_main(args)
+        return
+    cfg = CONFIGS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    timer = Timer()
+    head = measure(cfg, args, dev, timer, headline=True)
+    step = head.pop("_step")
+    fns = head.pop("_fns")
+    decode, out = fns["decode"], fns["out"]
+    launch_ms = timer.launch_ms
 
     # copy-on-write copies (pa_copy_blocks): up to 1024 pairs from blocks the
     # batch uses into free blocks, so no table's data changes
@@ -351,21 +460,18 @@ def main():
                                   tail_waste_tokens=int((nbs * B - L).sum()))
             del kb, vb
 
-    dec_cold = copy_gbs = None
+    copy_gbs = None
     if args.extras:
-        evict = torch.ones(192 << 20, dtype=torch.float32, device=dev)  # 768 MiB
-        dec_cold = cold_us(decode, evict)
-        del evict
         # bandwidth context: a plain 1 GiB device copy (reads and writes 1 GiB)
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
         dst.copy_(src)
-        e0.record()
+        timer.e0.record()
         for _ in range(5):
             dst.copy_(src)
-        e1.record()
+        timer.e1.record()
         torch.cuda.synchronize()
-        copy_gbs = round(2 * (1 << 30) * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
+        copy_gbs = round(2 * (1 << 30) * 5 / (timer.e0.elapsed_time(timer.e1) * 1e-3) / 1e9, 1)
         del src, dst
     if args.copy_probe_mib:
         # a plain device copy of known size: rocprofv3 --pmc reads of FETCH_SIZE /
@@ -375,12 +481,8 @@ def main():
         dst = torch.empty_like(src)
         dst.copy_(src)
         torch.cuda.synchronize()
+        del src, dst
 
-    tokens_per_step = cfg.num_seqs + (cfg.prefill_chunk if out_pre is not None else 0)
-    ab = algorithmic_bytes(cfg, step)
-    uniq = unique_kv_bytes(cfg, step)
-    kv_gbs = ab["kv"] / (ms_per_step * 1e-3) / 1e9
-    achieved = ab["total"] / (dec_ms * 1e-3) / 1e9
     traffic = None
     if os.path.exists(args.traffic_json):
         from paged_kv_cache_157_amd.rocprof_summary import decode_source_hash
@@ -391,56 +493,72 @@ def main():
         except (OSError, ValueError):
             traffic = None
 
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(cfg, step)
+    del step, out, decode, fns
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+    # the other workloads, one after another (each freed before the next)
+    subs = {}
+    if not args.no_configs:
+        for name in ("mha13b_prefix", "skew_splitk", "mixed_bf16", "mixed_fp8"):
+            if name == cfg.name:
+                continue
+            subs[name] = measure(CONFIGS[name], args, dev, timer, headline=False)
+            torch.cuda.synchronize()
+            torch.cuda.empty_cache()
+
+    dec_us = head["decode_us"]
+    cold = head.get("decode_cold")
     res = {
         "metric": METRIC,
-        "value": round(kv_gbs, 2),
+        "value": head["step_kv_gbs"],
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": cfg.cache_dtype,
         "data": "synthetic",
-        "config": {"workload": f"{cfg.name}: {cfg.title}", "num_seqs": cfg.num_seqs,
+        "config": {"workload": head["workload"], "num_seqs": cfg.num_seqs,
                    "q_heads": cfg.num_q_heads, "kv_heads": cfg.num_kv_heads,
                    "head_dim": cfg.head_dim, "block_size": 16, "pool_blocks": cfg.num_blocks,
-                   "context_tokens": int(step.plan.context_lens.sum()),
-                   "new_tokens": int(len(step.plan.slot_mapping)), "seed": cfg.seed},
-        "pct_of_hbm_peak": round(100.0 * kv_gbs / HBM_PEAK_GBS, 2),
-        "tokens_per_step": tokens_per_step,
-        "tokens_per_s": round(tokens_per_step / (ms_per_step * 1e-3), 1),
-        "decode_us": round(dec_ms * 1e3, 2),
-        # with the Infinity Cache evicted before every launch (decode_us: warm)
-        "decode_cold_us": dec_cold,
-        "decode_cold_kv_gbs": (round(ab["kv"] / (dec_cold["median"] * 1e-6) / 1e9, 2)
-                               if dec_cold else None),
+                   "context_tokens": head["context_tokens"], "new_tokens": head["new_tokens"],
+                   "seed": cfg.seed},
+        "pct_of_hbm_peak": round(100.0 * head["step_kv_gbs"] / HBM_PEAK_GBS, 2),
+        "tokens_per_step": head["tokens_per_step"],
+        "tokens_per_s": head["tokens_per_s"],
+        "decode_us": dec_us,
+        "decode_kv_gbs": head["decode_kv_gbs"],
+        "cache_write_us": head["cache_write_us"],
+        "roofline": {"bound": "hbm", "achieved": head["decode_achieved_gbs"], "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": head["decode_frac_of_hbm_peak"],
+                     "traffic": traffic,
+                     "kernel": f"pa_decode ({head['decode_kernel']}, one launch)",
+                     "algorithmic_bytes_per_launch": head["decode_algorithmic_bytes"],
+                     "timing": f"warm: {max(args.steps, TIMING_LAUNCHES)} back-to-back launches "
+                               f"after the timed steps, one HIP event pair, {dec_us} us per launch",
+                     "cold": None if cold is None else dict(
+                         cold, timing="Infinity Cache evicted before every launch (768 MiB read, "
+                                      "subtracted); median and minimum over 5 x 20 launches")},
         "device_copy_gbs": copy_gbs,
-        "cache_write_us": round(cw_ms * 1e3, 2),
         "copy_blocks": copy_res,
         "swap_blocks": swap_res,
         "block_size_sweep": bs_res,
-        "decode_kv_gbs": round(ab["kv"] / (dec_ms * 1e-3) / 1e9, 2),
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "kernel": f"pa_decode ({decode_kernel_name(cfg)}, one launch)",
-                     "algorithmic_bytes_per_launch": ab["total"]},
     }
-    if uniq < ab["kv"]:  # shared blocks: the distinct bytes read as well
-        res["unique_kv_bytes"] = uniq
-        res["decode_unique_kv_gbs"] = round(uniq / (dec_ms * 1e-3) / 1e9, 2)
-    if cfg.partition_tokens > 0:
-        res["partial_bytes_per_launch"] = partial_bytes(cfg, step)
-    if pre_ms is not None:
-        g = cfg.num_q_heads * cfg.head_dim * 4 * sum(
-            cfg.prefill_history + j + 1 for j in range(cfg.prefill_chunk))
-        res["prefill_us"] = round(pre_ms * 1e3, 2)
-        res["prefill_tflops"] = round(g / (pre_ms * 1e-3) / 1e12, 2)
-        res["prefill_pct_of_bf16_mfma_peak"] = round(100.0 * res["prefill_tflops"] / MFMA_BF16_PEAK_TFLOPS, 2)
-    if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(cfg, step)
+    for k in ("unique_kv_bytes", "decode_unique_kv_gbs", "partial_bytes_per_launch", "prefill_us",
+              "prefill_tflops", "prefill_pct_of_bf16_mfma_peak"):
+        if k in head:
+            res[k] = head[k]
+    if subs:
+        res["configs"] = subs
+    if cpu is not None:
+        res["cpu_baseline"] = cpu
     print(json.dumps(res), flush=True)
 
 
