@@ -185,6 +185,29 @@ pa_status pa_decode(float *out, const void *q, const void *k_cache, const void *
                     const pa_shape *shape, void *workspace, size_t workspace_bytes,
                     void *stream);
 
+/*
+ * pa_decode_static -- pa_decode without a caller workspace, for callers that
+ *   cannot allocate device memory (code under HIP graph capture, serving
+ *   loops and harnesses that forbid allocation).  Same arguments, result and
+ *   errors as pa_decode, minus the workspace: the arrival counters and split-K
+ *   partial records live in a static device array of the library (32 MiB per
+ *   device, held until the process ends: 1 MiB of counters, then the partial
+ *   records).  The call allocates nothing; its first call on a device resolves
+ *   the array's address and queues a fill kernel on `stream` that zeroes the
+ *   counters, and every call leaves them zero again.
+ *   Limits: num_seqs * num_kv_heads <= 2^18, and the shape's partial records
+ *   (pa_decode_workspace_bytes(shape) minus its 4 MiB of counters) must fit in
+ *   31 MiB, else PA_ERR_WORKSPACE before any launch.  The balanced split
+ *   (partition_tokens 0) needs (grid + S*Hkv) * G * (head_dim + 2) * 4 bytes,
+ *   a few MB for the usual batches; fixed partitions of long sequences can need
+ *   more.  All calls on one device share the array: calls that may overlap in
+ *   time (different streams, several host threads) race on it and must not
+ *   be issued; calls queued on one stream are safe.
+ */
+pa_status pa_decode_static(float *out, const void *q, const void *k_cache, const void *v_cache,
+                           const int32_t *block_tables, const int32_t *context_lens, float scale,
+                           const pa_shape *shape, void *stream);
+
 /* Workspace bytes pa_prefill_chunk needs for total_query_rows rows (depends
  * on the shape, the row count and the device's compute-unit count, which
  * sets how many key-range splits the call uses). */

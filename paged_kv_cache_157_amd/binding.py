@@ -64,6 +64,8 @@ def load() -> ctypes.CDLL:
         lib.pa_decode_workspace_bytes.restype = sz
         lib.pa_decode.argtypes = [P, P, P, P, P, P, f32, S, P, sz, P]
         lib.pa_decode.restype = ctypes.c_int
+        lib.pa_decode_static.argtypes = [P, P, P, P, P, P, f32, S, P]
+        lib.pa_decode_static.restype = ctypes.c_int
         lib.pa_prefill_workspace_bytes.argtypes = [S, i64]
         lib.pa_prefill_workspace_bytes.restype = sz
         lib.pa_prefill_chunk.argtypes = [P, P, P, P, P, P, P, i64, f32, S, P, sz, P]
@@ -260,6 +262,34 @@ def decode(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor, v_cache: t
     _check(lib.pa_decode(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
                          _ptr(context_lens), float(scale), ctypes.byref(shape), _ptr(ws),
                          0 if ws is None else ws.numel() * ws.element_size(), _stream(dev)))
+    return out
+
+
+def decode_static(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor,
+                  v_cache: torch.Tensor, block_tables: torch.Tensor, context_lens: torch.Tensor,
+                  scale: float, partition_tokens: int = 0, kv_scale: float = 1.0) -> torch.Tensor:
+    """pa_decode_static: pa_decode with the library's static device scratch
+    instead of a workspace (nothing is allocated).  Calls that may overlap in
+    time on one device must not be issued (they share that scratch)."""
+    dev = k_cache.device
+    _require(out, "out", dev, torch.float32, 3)
+    _require(q, "q", dev, None, 3)
+    _require(k_cache, "k_cache", dev)
+    _require(v_cache, "v_cache", dev)
+    _require(block_tables, "block_tables", dev, torch.int32, 2)
+    _require(context_lens, "context_lens", dev, torch.int32, 1)
+    S = q.shape[0]
+    if out.shape != q.shape or block_tables.shape[0] != S or context_lens.shape[0] != S:
+        raise ValueError("out/q/block_tables/context_lens disagree on the sequence count")
+    if v_cache.shape != k_cache.shape or v_cache.dtype != k_cache.dtype:
+        raise ValueError("k_cache and v_cache must match")
+    if q.shape[2] != k_cache.shape[3]:
+        raise ValueError("head_dim of q and of the pools differ")
+    shape = make_shape(q.shape[1], k_cache, q.dtype, S, block_tables.shape[1], kv_scale,
+                       partition_tokens)
+    _check(load().pa_decode_static(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                   _ptr(block_tables), _ptr(context_lens), float(scale),
+                                   ctypes.byref(shape), _stream(dev)))
     return out
 
 

@@ -177,18 +177,133 @@ struct DecodeLayout {
     size_t count_bytes, acc_bytes, ml_bytes, total;
 };
 
-DecodeLayout decode_layout(const pa_shape *s)
+// Decode workspace: arrival counters (counter_slots int32), then the split-K
+// partial records: (max, sum) pairs and accumulators.
+DecodeLayout decode_layout(const pa_shape *s, int64_t counter_slots = pa::kDecodeCounterSlots)
 {
     const int G = s->num_q_heads / s->num_kv_heads;
     const int pb = s->partition_tokens > 0 ? s->partition_tokens / 16 : 0;
     DecodeLayout L;
     L.slots = pa::decode_partial_slots(s->num_seqs, s->num_kv_heads, G, units_per_seq(s), pb,
                                        decode_grid(s), unit_shift(s));
-    L.count_bytes = (size_t)pa::kDecodeCounterSlots * sizeof(int32_t);
+    L.count_bytes = (size_t)counter_slots * sizeof(int32_t);
     L.ml_bytes = align256((size_t)L.slots * G * 2 * sizeof(float));
     L.acc_bytes = align256((size_t)L.slots * G * s->head_dim * sizeof(float));
     L.total = L.count_bytes + L.ml_bytes + L.acc_bytes;
     return L;
+}
+
+// Checks shared by the decode entry points; PA_OK means "launch".
+pa_status check_decode(const float *out, const void *q, const void *k_cache, const void *v_cache,
+                       const int32_t *block_tables, const int32_t *context_lens, float scale,
+                       const pa_shape *shape, int64_t counter_slots)
+{
+    pa_status st = check_shape(shape, true);
+    if (st != PA_OK)
+        return st;
+    const int G = shape->num_q_heads / shape->num_kv_heads;
+    if (shape->q_dtype != q_dtype_for(shape->cache_dtype))
+        return fail(PA_ERR_UNSUPPORTED, "q_dtype %d with cache_dtype %d", shape->q_dtype,
+                    shape->cache_dtype);
+    if (!pa::decode_supported(shape->cache_dtype, shape->head_dim, G))
+        return fail(PA_ERR_UNSUPPORTED, "decode not built for cache_dtype %d, head_dim %d, G %d",
+                    shape->cache_dtype, shape->head_dim, G);
+    if (shape->partition_tokens < 0 || shape->partition_tokens % 16 != 0)
+        return fail(PA_ERR_INVALID, "partition_tokens must be 0 or a positive multiple of 16");
+    if (!std::isfinite(scale))
+        return fail(PA_ERR_INVALID, "scale is not finite");
+    if ((int64_t)shape->num_seqs * shape->num_kv_heads > counter_slots)
+        return fail(PA_ERR_UNSUPPORTED, "num_seqs * num_kv_heads above %lld",
+                    (long long)counter_slots);
+    if (shape->num_seqs > 0 && (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens))
+        return fail(PA_ERR_INVALID, "NULL data pointer");
+    return PA_OK;
+}
+
+// One decode launch over a workspace laid out by decode_layout(shape, L).
+pa_status launch_decode_on(float *out, const void *q, const void *k_cache, const void *v_cache,
+                           const int32_t *block_tables, const int32_t *context_lens, float scale,
+                           const pa_shape *shape, char *ws, const DecodeLayout &L, void *stream)
+{
+    pa::DecodeArgs a;
+    a.out = out;
+    a.q = q;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.block_tables = block_tables;
+    a.context_lens = context_lens;
+    a.num_seqs = shape->num_seqs;
+    a.num_q_heads = shape->num_q_heads;
+    a.num_kv_heads = shape->num_kv_heads;
+    a.head_dim = shape->head_dim;
+    a.max_blocks = shape->max_blocks_per_seq;
+    a.tbs_log2 = unit_shift(shape);
+    a.num_blocks = kernel_blocks(shape);
+    a.cache_dtype = shape->cache_dtype;
+    a.part_blocks = shape->partition_tokens / 16;
+    // Fixed partitions are whole work items, so static ranges of them cannot
+    // balance; three times the resident work-groups lets the dispatcher hand
+    // the later ones to the CUs that finish first (measured: 2x and 4-8x are
+    // slower on the 32k/short skewed batch; the balanced split balances by
+    // itself and loses with any oversubscription).
+    a.grid = decode_grid(shape) * (shape->partition_tokens > 0 ? kPartitionGridFactor : 1);
+    const float kvs = kv_scale_of(shape);
+    a.qk_scale = scale * 1.4426950408889634f * kvs;
+    a.v_scale = kvs;
+    a.ws_count = (int32_t *)ws;
+    a.ws_ml = (float *)(ws + L.count_bytes);
+    a.ws_acc = (float *)(ws + L.count_bytes + L.ml_bytes);
+    hipError_t e = pa::launch_decode(a, (hipStream_t)stream);
+    return e == hipSuccess ? ok() : hip_fail(e, "decode launch");
+}
+
+// ---------------------------------------------------------------------------
+// Scratch of pa_decode_static: one array per device, for callers that cannot
+// allocate.  Arrival counters first (a fixed region, so that a later call with
+// more (sequence, KV head) pairs never takes an earlier call's partial results
+// for counters), then the partial records.
+// ---------------------------------------------------------------------------
+constexpr size_t kStaticScratchBytes = (size_t)32 << 20;
+constexpr int64_t kStaticCounterSlots = (int64_t)1 << 18;  // 1 MiB of int32 counters
+static_assert((size_t)kStaticCounterSlots * 4 < kStaticScratchBytes, "scratch layout");
+
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+__global__ void zero_counters_kernel(int32_t *p, int64_t n)
+{
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+         i += (int64_t)gridDim.x * blockDim.x)
+        p[i] = 0;
+}
+
+// Device address of `scratch` on the current device (the array's name is only
+// a host-side stand-in), resolved once per device; the first call also queues
+// a fill kernel on `stream` that zeroes the counter region.  Afterwards every
+// decode leaves its counters zero again.
+pa_status static_scratch(void *stream, char **out)
+{
+    static std::mutex mu;
+    static void *addr[64] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= 64)
+        return fail(PA_ERR_UNSUPPORTED, "device id %d above 63", dev);
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return hip_fail(e != hipSuccess ? e : hipErrorInvalidSymbol, "hipGetSymbolAddress(scratch)");
+        zero_counters_kernel<<<256, 256, 0, (hipStream_t)stream>>>((int32_t *)p, kStaticCounterSlots);
+        e = hipGetLastError();
+        if (e != hipSuccess)
+            return hip_fail(e, "zeroing the static scratch counters");
+        addr[dev] = p;
+    }
+    *out = (char *)addr[dev];
+    return PA_OK;
 }
 
 }  // namespace
@@ -320,62 +435,41 @@ pa_status pa_decode(float *out, const void *q, const void *k_cache, const void *
                     const int32_t *block_tables, const int32_t *context_lens, float scale,
                     const pa_shape *shape, void *workspace, size_t workspace_bytes, void *stream)
 {
-    pa_status st = check_shape(shape, true);
+    pa_status st = check_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, shape,
+                                pa::kDecodeCounterSlots);
     if (st != PA_OK)
         return st;
-    const int G = shape->num_q_heads / shape->num_kv_heads;
-    if (shape->q_dtype != q_dtype_for(shape->cache_dtype))
-        return fail(PA_ERR_UNSUPPORTED, "q_dtype %d with cache_dtype %d", shape->q_dtype,
-                    shape->cache_dtype);
-    if (!pa::decode_supported(shape->cache_dtype, shape->head_dim, G))
-        return fail(PA_ERR_UNSUPPORTED, "decode not built for cache_dtype %d, head_dim %d, G %d",
-                    shape->cache_dtype, shape->head_dim, G);
-    if (shape->partition_tokens < 0 || shape->partition_tokens % 16 != 0)
-        return fail(PA_ERR_INVALID, "partition_tokens must be 0 or a positive multiple of 16");
-    if (!std::isfinite(scale))
-        return fail(PA_ERR_INVALID, "scale is not finite");
-    if ((int64_t)shape->num_seqs * shape->num_kv_heads > pa::kDecodeCounterSlots)
-        return fail(PA_ERR_UNSUPPORTED, "num_seqs * num_kv_heads above %lld",
-                    (long long)pa::kDecodeCounterSlots);
     if (shape->num_seqs == 0)
         return ok();
-    if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
-        return fail(PA_ERR_INVALID, "NULL data pointer");
     const DecodeLayout L = decode_layout(shape);
     if (!workspace || workspace_bytes < L.total)
         return fail(PA_ERR_WORKSPACE, "decode needs %zu workspace bytes, got %zu", L.total,
                     workspace ? workspace_bytes : (size_t)0);
-    pa::DecodeArgs a;
-    a.out = out;
-    a.q = q;
-    a.k_cache = k_cache;
-    a.v_cache = v_cache;
-    a.block_tables = block_tables;
-    a.context_lens = context_lens;
-    a.num_seqs = shape->num_seqs;
-    a.num_q_heads = shape->num_q_heads;
-    a.num_kv_heads = shape->num_kv_heads;
-    a.head_dim = shape->head_dim;
-    a.max_blocks = shape->max_blocks_per_seq;
-    a.tbs_log2 = unit_shift(shape);
-    a.num_blocks = kernel_blocks(shape);
-    a.cache_dtype = shape->cache_dtype;
-    a.part_blocks = shape->partition_tokens / 16;
-    // Fixed partitions are whole work items, so static ranges of them cannot
-    // balance; three times the resident work-groups lets the dispatcher hand
-    // the later ones to the CUs that finish first (measured: 2x and 4-8x are
-    // slower on the 32k/short skewed batch; the balanced split balances by
-    // itself and loses with any oversubscription).
-    a.grid = decode_grid(shape) * (shape->partition_tokens > 0 ? kPartitionGridFactor : 1);
-    const float kvs = kv_scale_of(shape);
-    a.qk_scale = scale * 1.4426950408889634f * kvs;
-    a.v_scale = kvs;
-    char *ws = (char *)workspace;
-    a.ws_count = (int32_t *)ws;
-    a.ws_ml = (float *)(ws + L.count_bytes);
-    a.ws_acc = (float *)(ws + L.count_bytes + L.ml_bytes);
-    hipError_t e = pa::launch_decode(a, (hipStream_t)stream);
-    return e == hipSuccess ? ok() : hip_fail(e, "decode launch");
+    return launch_decode_on(out, q, k_cache, v_cache, block_tables, context_lens, scale, shape,
+                            (char *)workspace, L, stream);
+}
+
+pa_status pa_decode_static(float *out, const void *q, const void *k_cache, const void *v_cache,
+                           const int32_t *block_tables, const int32_t *context_lens, float scale,
+                           const pa_shape *shape, void *stream)
+{
+    pa_status st = check_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, shape,
+                                kStaticCounterSlots);
+    if (st != PA_OK)
+        return st;
+    if (shape->num_seqs == 0)
+        return ok();
+    const DecodeLayout L = decode_layout(shape, kStaticCounterSlots);
+    if (L.total > kStaticScratchBytes)
+        return fail(PA_ERR_WORKSPACE,
+                    "decode of this shape needs %zu scratch bytes; the static scratch holds %zu "
+                    "(use pa_decode with a workspace)", L.total, kStaticScratchBytes);
+    char *ws = nullptr;
+    st = static_scratch(stream, &ws);
+    if (st != PA_OK)
+        return st;
+    return launch_decode_on(out, q, k_cache, v_cache, block_tables, context_lens, scale, shape, ws,
+                            L, stream);
 }
 
 size_t pa_prefill_workspace_bytes(const pa_shape *shape, int64_t total_query_rows)
