@@ -1,12 +1,13 @@
-// decode.hip -- single-query decode attention over a paged KV cache.
+// decode.hip -- single-query decode attention over a paged KV cache, one KV
+// head per work-group at a time (decode_hg.h holds the kernel that takes four
+// KV heads per work-group; this file also chooses between the two).
 //
 // What is computed ("Lecture 33" §2.3): for every sequence i and query head
 // h, out[i,h] = softmax(scale * q[i,h] K^T) V over the sequence's tokens,
 // whose K/V rows are read in place from scattered physical blocks through
 // the block table (logical block t/16, offset t%16, §2.2 walk-through).  The
-// pages name a streaming (online) softmax and no more; the recurrence used
-// here is the standard one: running maximum, running sum, rescaled
-// accumulator, followed by a log-sum-exp merge of partial results.
+// lane geometry, the start-up scan, the partial-record slots and the merge are
+// in decode_common.h, shared with decode_hg.h.
 //
 // Work decomposition (MI355X: 256 CUs in 8 XCDs, wave64):
 //   * The flat list of "items" is (sequence, KV head, x) where x is a
@@ -36,8 +37,7 @@
 //   * PV: probabilities go through a 512-byte LDS buffer to the lanes holding
 //     V; each lane owns one 16-byte chunk of V for four tokens of the block
 //     and accumulates G fp32 heads with FMA.
-#include "pa_device.h"
-#include "pa_internal.h"
+#include "decode_common.h"
 
 namespace pa {
 
@@ -55,130 +55,9 @@ namespace pa {
 #define DECODE_WAVES 4   // waves per work-group; they split a segment's blocks
 #endif
 
-template <int CDT, int D, int G>
-struct DecodeCfg {
-    static constexpr int EB = Storage<CDT>::bytes;
-    static constexpr int E = 16 / EB;            // cache elements per 16-byte chunk
-    static constexpr int NC = D / E;             // chunks in one token row of one head
-    static constexpr int LPT = G <= 4 ? 4 : 8;   // QK lanes per token
-    static constexpr int GP = G <= 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : 8;
-    static constexpr int CPL = NC / LPT;         // K chunks per lane and token
-    static constexpr int ROUNDS = LPT / 4;       // QK passes per 16-token block
-    static constexpr int TRN = 4 / ROUNDS;       // tokens per row per QK pass
-    static constexpr int VTPR = 16 / NC;         // tokens per row per V pass
-    static constexpr int VPASS = 4 / VTPR;       // V passes per block
-    // q dwords per (head slot, K chunk): bf16 pairs matching the chunk, or fp32
-    static constexpr int QW = CDT == DT_FP8 ? 8 : 4;
-    static_assert(CPL >= 1 && NC <= 16 && NC >= 4, "unsupported chunk geometry");
-    static_assert(G >= 1 && G <= 8, "GQA group must be 1..8");
-};
-
-// Token (0..15 within the block) held in "row" r at index k (0..3).  QK lanes
-// of row r handle exactly the tokens that the V lanes of row r accumulate, so
-// the running maximum of a row never has to leave it.
-template <int LPT>
-__device__ __forceinline__ int row_token(int r, int k)
-{
-    if constexpr (LPT == 4)
-        return 4 * r + k;
-    else
-        return 2 * r + (k & 1) + 8 * (k >> 1);
-}
-
-// Reduce-scatter of GP partial sums over the LPT lanes of one token.  On
-// entry slot s of a lane holds the partial sum of head (s ^ mask); on exit
-// x[0] holds the complete sum of head `mask`.
-template <int LPT, int GP>
-__device__ __forceinline__ float reduce_scatter(float (&x)[GP])
-{
-    if constexpr (LPT == 8) {
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-            x[k] += dpp<DPP_HALF_MIRROR>(x[k + 4]);
-#pragma unroll
-        for (int k = 0; k < 2; ++k)
-            x[k] += dpp<DPP_QP_X1>(x[k + 2]);
-        x[0] += dpp<DPP_QP_X2>(x[1]);
-    } else if constexpr (GP == 4) {
-#pragma unroll
-        for (int k = 0; k < 2; ++k)
-            x[k] += dpp<DPP_QP_X1>(x[k + 2]);
-        x[0] += dpp<DPP_QP_X2>(x[1]);
-    } else if constexpr (GP == 2) {
-        x[0] += dpp<DPP_QP_X1>(x[1]);
-        x[0] += dpp<DPP_QP_X2>(x[0]);
-    } else {
-        x[0] += dpp<DPP_QP_X1>(x[0]);
-        x[0] += dpp<DPP_QP_X2>(x[0]);
-    }
-    return x[0];
-}
-
-// Head handled by a lane after reduce_scatter, and whether the lane is the
-// single owner of that (token, head) value (others hold copies).
-template <int LPT, int GP>
-__device__ __forceinline__ int head_mask(int lane)
-{
-    const int b0 = lane & 1, b1 = (lane >> 1) & 1, b2 = (lane >> 2) & 1;
-    if constexpr (LPT == 8)
-        return 4 * b2 + 2 * (b0 ^ b2) + (b1 ^ b2);
-    else if constexpr (GP == 4)
-        return 2 * b0 + b1;
-    else if constexpr (GP == 2)
-        return b0;
-    else
-        return 0;
-}
-template <int LPT, int GP>
-__device__ __forceinline__ bool mask_owner(int lane)
-{
-    if constexpr (LPT == 8 || GP == 4)
-        return true;
-    else if constexpr (GP == 2)
-        return ((lane >> 1) & 1) == 0;
-    else
-        return (lane & 3) == 0;
-}
-
-// Sum over the 64 lanes of a wave.
-__device__ __forceinline__ long long wave_sum64(long long v)
-{
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1)
-        v += __shfl_xor(v, d);
-    return v;
-}
-
-// Sum of a value over the 64 lanes that share a "column" pattern: lanes that
-// differ only in the row (bits 4-5) and in the bits selected by the pattern.
-// gfx950's lane swaps exchange the wave halves (rows 0-1 <-> 2-3) and
-// neighbouring rows in registers: swapping a value with itself leaves
-// {v(l), v(l ^ 32)} (then {v(l), v(l ^ 16)}) in the two results of every
-// lane l.
-__device__ __forceinline__ float sum_rows(float v)
-{
-    const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    v = __uint_as_float(h[0]) + __uint_as_float(h[1]);
-    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-// Inclusive prefix sum over the 64 lanes of a wave (32-bit): shifts within
-// rows of 16, then the row totals carried over with row broadcasts.
-__device__ __forceinline__ int wave_scan32(int x)
-{
-    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, true);  // row_shr:1
-    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, true);  // row_shr:2
-    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, true);  // row_shr:4
-    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, true);  // row_shr:8
-    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false); // row_bcast:15 into rows 1, 3
-    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false); // row_bcast:31 into rows 2, 3
-    return x;
-}
-
 template <int CDT, int D, int G, int NSTAGE, int WAVES>
 struct DecodeSmem {
-    using C = DecodeCfg<CDT, D, G>;
+    using C = dec::DecodeCfg<CDT, D, G>;
     static constexpr int KB = 16 * D * C::EB;  // bytes of one block of one KV head (K or V)
     // bytes of the q rows of one (sequence, KV head): G heads x D (fp32 q with
     // an fp32 cache, else bf16), rounded up to whole 1 KiB DMA instructions
@@ -192,25 +71,10 @@ struct DecodeSmem {
     float p[WAVES][16][8];       // probabilities of the current block
     float bmax[WAVES][4][8];     // row maxima (rescale path)
     float msum[WAVES][2][8];     // per-wave running max and sum
-    long long total;  // item count of the call (start-up scan)
-    long long total_v;  // the same in virtual items (0: plain split)
-    long long range0, range1;  // this work-group's items [range0, range1)
+    dec::Range range;            // this work-group's range (start-up scan)
+    dec::MergeLds<G, 8> merge;   // merge of one (sequence, KV head)
     int last;
-    int seg_i;
-    long long seg_base, seg_vbase;
 };
-
-// s_waitcnt vmcnt(N): the global->LDS loads of the ring are counted there and
-// the compiler does not wait for them by itself.
-template <int N>
-__device__ __forceinline__ void wait_vm()
-{
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-// Work-group barrier for LDS data only: every wave's LDS accesses have
-// completed (lgkmcnt), global loads may stay in flight.  Where a hand-over
-// needs global memory complete, the code waits for it explicitly first.
-__device__ __forceinline__ void barrier_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 __device__ __forceinline__ void dma16(const void *src, void *lds_dst)
 {
@@ -222,11 +86,14 @@ __device__ __forceinline__ void dma16(const void *src, void *lds_dst)
 template <int CDT, int D, int G, int NSTAGE, int WAVES, bool H8>
 __global__ __launch_bounds__(64 * WAVES) void decode_kernel(DecodeArgs a)
 {
-    using C = DecodeCfg<CDT, D, G>;
+    using C = dec::DecodeCfg<CDT, D, G>;
     using SM = DecodeSmem<CDT, D, G, NSTAGE, WAVES>;
+    using dec::row_token;
+    using dec::wait_vm;
+    using dec::barrier_lds;
     constexpr int NT = 64 * WAVES;
     constexpr int LPT = C::LPT, GP = C::GP, CPL = C::CPL, ROUNDS = C::ROUNDS;
-    constexpr int NC = C::NC, E = C::E, VTPR = C::VTPR, VPASS = C::VPASS, QW = C::QW;
+    constexpr int EV = C::EV, NCV = C::NCV, E = C::E, VTPR = C::VTPR, VPASS = C::VPASS, QW = C::QW;
     constexpr int KB = SM::KB;
     constexpr int LPB = 2 * KB / 1024;  // DMA instructions per block (K and V)
     static_assert(ROUNDS * CPL * 1024 == KB && VPASS * 1024 == KB, "DMA layout");
@@ -260,188 +127,40 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(DecodeArgs a)
         return Phys{e, e};
     };
 
-    auto items_of = [&](int L) -> int {
-        L = L < 0 ? 0 : L;
-        int nb = (L + 15) >> 4;
-        nb = nb > maxU ? maxU : nb;
-        return PB > 0 ? (nb + PB - 1) / PB : nb;
-    };
-
-    // ---- this work-group's range of items.  With the balanced split the
-    // ranges are equal in "virtual" items: each (sequence, KV head) counts
-    // ALPHA extra items ahead of its real ones (what a segment start costs),
-    // so a range that starts segments holds fewer real items.  Wave 0 scans
-    // the lengths 64 at a time (no work-group barrier inside), finds the
-    // sequences holding both ends of its range and the first real items at or
-    // after them; the other waves wait at the barrier below.
+    // ---- this work-group's range of items (balanced split: equal in virtual
+    // items, ALPHA per (sequence, KV head)); wave 0 scans, the others wait at
+    // the barrier below
     constexpr int ALPHA = DECODE_SEGCOST;
     if (w == 0) {
-        const long long W = gridDim.x;
-        // 64 lanes' item counts fit 32 bits whenever (maxU + ALPHA) * Hkv * 64
-        // does: DPP scans then; otherwise shuffles on 64-bit values
-        const bool narrow = (long long)(maxU + ALPHA) * Hkv * 64 < (1ll << 31);
-        auto scan = [&](long long v) -> long long {
-            if (narrow)
-                return wave_scan32((int)v);
-            long long incl = v;
-#pragma unroll
-            for (int d = 1; d < 64; d <<= 1) {
-                const long long t = __shfl_up(incl, d);
-                if (lane >= d)
-                    incl += t;
-            }
-            return incl;
-        };
-        auto counts = [&](int l, long long &real, long long &virt) {
-            const int n = items_of(l);
-            real = (long long)n * Hkv;
-            virt = (long long)(n > 0 ? n + ALPHA : 0) * Hkv;
-        };
-        long long tot = 0, totv = 0;
-        // up to 64 sequences with narrow counts: one load of the lengths and
-        // one pair of prefix sums serve the totals and the search below
-        const bool one_pass = narrow && S <= 64;
-        int l0 = 0, ri0 = 0, vi0 = 0;
-        long long rr0 = 0, vv0 = 0;
-        if (one_pass) {
-            l0 = lane < S ? a.context_lens[lane] : 0;
-            counts(l0, rr0, vv0);
-            ri0 = wave_scan32((int)rr0);
-            vi0 = wave_scan32((int)vv0);
-            tot = __builtin_amdgcn_readlane(ri0, 63);
-            totv = __builtin_amdgcn_readlane(vi0, 63);
-        } else {
-            for (int base = 0; base < S; base += 64) {
-                const int s2 = base + lane;
-                long long r, v;
-                counts(s2 < S ? a.context_lens[s2] : 0, r, v);
-                if (narrow) {
-                    tot += __builtin_amdgcn_readlane(wave_scan32((int)r), 63);
-                    totv += __builtin_amdgcn_readlane(wave_scan32((int)v), 63);
-                } else {
-                    tot += wave_sum64(r);
-                    totv += wave_sum64(v);
-                }
-            }
-        }
-        const bool virt = PB == 0 && ALPHA > 0 && totv >= (long long)(ALPHA + 2) * W;
-        // position x of the split -> (sequence, its real / virtual starts, first
-        // real item at or after x)
-        auto locate = [&](long long x, int &seq, long long &rbase, long long &vbase) -> long long {
-            const long long T = virt ? totv : tot;
-            seq = -1;
-            rbase = tot;
-            vbase = totv;
-            if (x >= T)
-                return tot;
-            long long rc = 0, vc = 0;
-            for (int base = 0; base < S; base += 64) {
-                const int s2 = base + lane;
-                const int l = s2 < S ? a.context_lens[s2] : 0;
-                long long r, v;
-                counts(l, r, v);
-                const long long ri = scan(r), vi = scan(v);
-                const long long ex = (virt ? vi - v : ri - r), in = virt ? vi : ri;
-                const long long c0 = virt ? vc : rc;
-                const unsigned long long m =
-                    __builtin_amdgcn_ballot_w64(r > 0 && c0 + ex <= x && x < c0 + in);
-                if (m) {
-                    const int l2 = __builtin_ctzll(m);
-                    seq = base + l2;
-                    rbase = rc + __shfl(ri - r, l2);
-                    vbase = vc + __shfl(vi - v, l2);
-                    const int n = items_of(__shfl(l, l2));
-                    if (!virt)
-                        return x;
-                    const long long rel = x - vbase;
-                    const long long gq = rel / (n + ALPHA), xv = rel - gq * (n + ALPHA);
-                    return rbase + gq * n + (xv > ALPHA ? xv - ALPHA : 0);
-                }
-                rc += __shfl(ri, 63);
-                vc += __shfl(vi, 63);
-            }
-            return tot;  // not reached while x < T
-        };
-        const long long T = virt ? totv : tot;
-        int seq0, seq1;
-        long long rb0, vb0, rb1, vb1;
-        long long r0, r1;
-        if (one_pass) {
-            // the prefix sums above, the found lane read with scalar lane
-            // reads; 32-bit divisions wherever the operands fit (T * W < 2^31:
-            // every position, count and quotient below is under T)
-            const int l = l0;
-            const long long rr = rr0, vv = vv0;
-            const int ri = ri0, vi = vi0;
-            const int n = items_of(l);
-            const bool d32 = T * W < (1ll << 31);
-            auto div = [&](long long num, long long den) -> long long {
-                return d32 ? (long long)((unsigned)num / (unsigned)den) : num / den;
-            };
-            auto find = [&](long long x, int &seq, long long &rbase, long long &vbase) -> long long {
-                seq = -1;
-                rbase = tot;
-                vbase = totv;
-                if (x >= T)
-                    return tot;
-                const long long in = virt ? vi : ri, ex = in - (virt ? vv : rr);
-                const unsigned long long m = __builtin_amdgcn_ballot_w64(rr > 0 && ex <= x && x < in);
-                const int l2 = __builtin_ctzll(m);  // m != 0 while x < T
-                seq = l2;
-                rbase = __builtin_amdgcn_readlane(ri, l2) - __builtin_amdgcn_readlane((int)rr, l2);
-                vbase = __builtin_amdgcn_readlane(vi, l2) - __builtin_amdgcn_readlane((int)vv, l2);
-                if (!virt)
-                    return x;
-                const int nn = __builtin_amdgcn_readlane(n, l2);
-                const long long rel = x - vbase;
-                const long long gq = div(rel, nn + ALPHA), xv = rel - gq * (nn + ALPHA);
-                return rbase + gq * nn + (xv > ALPHA ? xv - ALPHA : 0);
-            };
-            r0 = find(div(T * blockIdx.x, W), seq0, rb0, vb0);
-            r1 = find(div(T * (blockIdx.x + 1), W), seq1, rb1, vb1);
-        } else {
-            r0 = locate(T * blockIdx.x / W, seq0, rb0, vb0);
-            r1 = locate(T * (blockIdx.x + 1) / W, seq1, rb1, vb1);
-        }
-        if (lane == 0) {
-            sm.total = tot;
-            sm.total_v = virt ? totv : 0;
-            sm.range0 = r0;
-            sm.range1 = r1;
-            sm.seg_i = seq0;
-            sm.seg_base = rb0;
-            sm.seg_vbase = vb0;
-        }
+        const dec::Range R = dec::startup_scan<ALPHA>(a.context_lens, S, Hkv, maxU, PB, lane);
+        if (lane == 0)
+            sm.range = R;
     }
     barrier_lds();
-    const long long total = uniform64(sm.total);
-    const long long total_v = uniform64(sm.total_v);  // > 0: virtual split
-    if (blockIdx.x == 0) {  // sequences with no tokens get a zero output row
-        for (int i = tid; i < S; i += NT)
-            if (a.context_lens[i] <= 0)
-                for (int e = 0; e < Hq * D; ++e)
-                    a.out[(int64_t)i * Hq * D + e] = 0.f;
-    }
-    const long long a0 = uniform64(sm.range0);
-    const long long a1 = uniform64(sm.range1);
+    dec::Range R;
+    R.total = uniform64(sm.range.total);
+    R.total_v = uniform64(sm.range.total_v);  // > 0: virtual split
+    dec::zero_empty_rows<D, NT>(a.context_lens, a.out, S, Hq, tid);
+    const long long a0 = uniform64(sm.range.r0);
+    const long long a1 = uniform64(sm.range.r1);
     if (a0 >= a1)
         return;
-    int i = uniform(sm.seg_i);
+    int i = uniform(sm.range.seq);
     if (i < 0)  // unreachable while a0 < total; keeps every index in range
         return;
-    long long base_i = uniform64(sm.seg_base);    // first item index of sequence i
-    long long vbase_i = uniform64(sm.seg_vbase);  // its first virtual item
+    long long base_i = uniform64(sm.range.base);    // first item index of sequence i
+    long long vbase_i = uniform64(sm.range.vbase);  // its first virtual item
     long long item = a0;
-    const int lane_m = head_mask<LPT, GP>(lane);
-    const bool lane_owner = mask_owner<LPT, GP>(lane) && lane_m < G;
+    const int lane_m = dec::head_mask<LPT, GP>(lane);
+    const bool lane_owner = dec::mask_owner<LPT, GP>(lane) && lane_m < G;
     const int row = lane >> 4;
 
     // QK lane geometry
     const int gl = lane & (LPT - 1);
     const int tr = LPT == 8 ? (lane >> 3) & 1 : (lane >> 2) & 3;
     // V lane geometry
-    const int vc = (lane & 15) % NC;
-    const int vh = (lane & 15) / NC;
+    const int vc = (lane & 15) % NCV;
+    const int vh = (lane & 15) / NCV;
 
     const int64_t tok_bytes = (int64_t)Hkv * D * C::EB;
     const int64_t blk_bytes = 16 * tok_bytes;
@@ -491,11 +210,11 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(DecodeArgs a)
     auto describe = [&](long long it, int &si, long long sbase) -> Seg {
         Seg d;
         int L = lens_s[si];
-        int n = items_of(L);
+        int n = dec::items_of(L, maxU, PB);
         while (n == 0) {  // cannot happen for the first segment; skip empties
             ++si;
             L = lens_s[si];
-            n = items_of(L);
+            n = dec::items_of(L, maxU, PB);
         }
         d.L = uniform(L > maxL ? maxL : L);
         d.n_i = uniform(n);
@@ -513,12 +232,7 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(DecodeArgs a)
             d.seg_items = (int)((long long)(d.n_i - d.x) < left ? (d.n_i - d.x) : left);
             d.b0 = d.x;
             d.b1 = d.x + d.seg_items;
-            // rank of this work-group among those with a non-empty range: with at
-            // least as many items as work-groups every range is non-empty (rank =
-            // blockIdx.x); with fewer, each non-empty range holds one item (rank =
-            // a0).  Ranks keep the partial slots of one (sequence, head) contiguous.
-            d.slot = (int)(total_v > 0 || a0 >= (long long)blockIdx.x ? (long long)blockIdx.x : a0) +
-                     si * Hkv + d.g;
+            d.slot = dec::partial_slot(a0, si * Hkv + d.g);
         }
         d.b0 = uniform(d.b0);
         d.b1 = uniform(d.b1);
@@ -555,31 +269,7 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(DecodeArgs a)
         return true;
     };
 
-    // Issue priority follows this wave's remaining work (3 at the start, 0 near
-    // the end): when two work-groups share a CU, the one that has fallen behind
-    // gets the instruction slots, instead of the older one by default, so both
-    // finish together.  The persistent grid fills every CU's first slot with
-    // work-groups [0, grid/2) before the second; the later ones lower their
-    // priority half a step later, which cancels the age tie-break at equal
-    // progress.  Only the order of issue changes, never the arithmetic.
-    const int exp_w = (int)((a1 - a0 + WAVES - 1) / WAVES);  // this wave's share, blocks
-    const int ew = exp_w > 0 ? exp_w : 1;
-    const int lag = blockIdx.x >= gridDim.x / 2 ? ew / 2 : 0;
-    int done_w = 0, cur_prio = -1;
-    auto update_priority = [&]() {
-        const int pr = 3 - min(3, max(0, 4 * done_w - lag) / ew);
-        if (pr != cur_prio) {
-            cur_prio = pr;
-            if (pr == 3)
-                __builtin_amdgcn_s_setprio(3);
-            else if (pr == 2)
-                __builtin_amdgcn_s_setprio(2);
-            else if (pr == 1)
-                __builtin_amdgcn_s_setprio(1);
-            else
-                __builtin_amdgcn_s_setprio(0);
-        }
-    };
+    dec::IssuePriority prio((int)((a1 - a0 + WAVES - 1) / WAVES));  // this wave's share, blocks
 
     // the first segment's q and each wave's first block go out together;
     // wave 0 then waits for q only
@@ -642,11 +332,11 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(DecodeArgs a)
         }
 
         // ---- per-wave streaming softmax over blocks b0+w, b0+w+WAVES, ... ---
-        float acc[G][E];
+        float acc[G][EV];
 #pragma unroll
         for (int h = 0; h < G; ++h)
 #pragma unroll
-            for (int e = 0; e < E; ++e)
+            for (int e = 0; e < EV; ++e)
                 acc[h][e] = 0.f;
         float mref[G];
 #pragma unroll
@@ -696,8 +386,7 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(DecodeArgs a)
         }
 
         for (int t = 0; t < nb_w; ++t) {
-            update_priority();
-            ++done_w;
+            prio.step();
             const int b = b0 + w + WAVES * t;
             const bool more1 = t + 1 < nb_w, more2 = t + 2 < nb_w;  // uniform
             const Phys pb2 = more2 ? unit_u(b + 2 * WAVES) : Phys{0, 0};
@@ -720,34 +409,11 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(DecodeArgs a)
 #pragma unroll
                 for (int c = 0; c < CPL; ++c) {
                     const u32x4 kc = *(const u32x4 *)(st + (j * CPL + c) * 1024);
-                    if constexpr (CDT == DT_BF16) {
 #pragma unroll
-                        for (int s = 0; s < GP; ++s)
-#pragma unroll
-                            for (int p = 0; p < 4; ++p)
-                                xs[s] = dot2_bf16(qr[s][c][p], kc[p], xs[s]);
-                    } else if constexpr (CDT == DT_FP8) {
-                        uint32_t kk[8];
-#pragma unroll
-                        for (int p = 0; p < 4; ++p) {
-                            kk[2 * p] = fp8x2_to_bf16x2<false>(kc[p]);
-                            kk[2 * p + 1] = fp8x2_to_bf16x2<true>(kc[p]);
-                        }
-#pragma unroll
-                        for (int s = 0; s < GP; ++s)
-#pragma unroll
-                            for (int p = 0; p < 8; ++p)
-                                xs[s] = dot2_bf16(qr[s][c][p], kk[p], xs[s]);
-                    } else {
-#pragma unroll
-                        for (int s = 0; s < GP; ++s)
-#pragma unroll
-                            for (int p = 0; p < 4; ++p)
-                                xs[s] = fmaf(__uint_as_float(qr[s][c][p]), __uint_as_float(kc[p]),
-                                             xs[s]);
-                    }
+                    for (int s = 0; s < GP; ++s)
+                        xs[s] = dec::dot_chunk<CDT, QW>(qr[s][c], kc, xs[s]);
                 }
-                const float s2 = reduce_scatter<LPT, GP>(xs) * a.qk_scale;
+                const float s2 = dec::reduce_scatter<LPT, GP>(xs) * a.qk_scale;
                 const int tt = tbase + row_token<LPT>(row, tr + j * C::TRN);
                 sc[j] = tt < L ? s2 : -INFINITY;
             }
@@ -781,7 +447,7 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(DecodeArgs a)
                     const float mnew = fmaxf(mref[h], mx);
                     const float alpha = mnew == -INFINITY ? 1.f : fast_exp2(mref[h] - mnew);
 #pragma unroll
-                    for (int e = 0; e < E; ++e)
+                    for (int e = 0; e < EV; ++e)
                         acc[h][e] *= alpha;
                     if (h == lane_m) {
                         my_alpha = alpha;
@@ -829,37 +495,16 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(DecodeArgs a)
 #pragma unroll
             for (int v = 0; v < VPASS; ++v) {
                 const int tk = row_token<LPT>(row, v * VTPR + vh);
-                const u32x4 vv = vrow[v];
                 float pr[G];
 #pragma unroll
                 for (int h = 0; h < G; ++h)
                     pr[h] = sm.p[w][tk][h];
-                float ve[E];
-                if constexpr (CDT == DT_BF16) {
-#pragma unroll
-                    for (int k = 0; k < 4; ++k) {
-                        ve[2 * k] = bf16_lo(vv[k]);
-                        ve[2 * k + 1] = bf16_hi(vv[k]);
-                    }
-                } else if constexpr (CDT == DT_FP8) {
-#pragma unroll
-                    for (int k = 0; k < 4; ++k) {
-                        const f32x2 lo = fp8x2_to_f32x2<false>(vv[k]);
-                        const f32x2 hi = fp8x2_to_f32x2<true>(vv[k]);
-                        ve[4 * k] = lo[0];
-                        ve[4 * k + 1] = lo[1];
-                        ve[4 * k + 2] = hi[0];
-                        ve[4 * k + 3] = hi[1];
-                    }
-                } else {
-#pragma unroll
-                    for (int k = 0; k < 4; ++k)
-                        ve[k] = __uint_as_float(vv[k]);
-                }
+                float ve[EV];
+                dec::widen_v<CDT, EV>(vrow[v], ve);
 #pragma unroll
                 for (int h = 0; h < G; ++h)
 #pragma unroll
-                    for (int e = 0; e < E; ++e)
+                    for (int e = 0; e < EV; ++e)
                         acc[h][e] = fmaf(pr[h], ve[e], acc[h][e]);
             }
             // V(t) is consumed: its half of the stage takes V(t+2)
@@ -883,32 +528,19 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(DecodeArgs a)
         }
 
         // ---- wave totals -> LDS --------------------------------------------
-        // sum over rows and over the lanes of a row that hold other tokens
-        float ls = lane_owner ? lsum : 0.f;
-        ls = sum_rows(ls);
-        if constexpr (LPT == 4)
-            ls += dpp<DPP_ROW_ROR4>(ls);
-        ls += dpp<DPP_ROW_ROR8>(ls);
+        const float ls = dec::token_total<LPT>(lane_owner ? lsum : 0.f);
 #pragma unroll
         for (int h = 0; h < G; ++h)
 #pragma unroll
-            for (int e = 0; e < E; ++e) {
-                float t = sum_rows(acc[h][e]);
-                if constexpr (VTPR == 2)
-                    t += dpp<DPP_ROW_ROR8>(t);
-                if constexpr (VTPR == 4) {
-                    t += dpp<DPP_ROW_ROR4>(t);
-                    t += dpp<DPP_ROW_ROR8>(t);
-                }
-                acc[h][e] = t;
-            }
-        if (lane < NC) {
+            for (int e = 0; e < EV; ++e)
+                acc[h][e] = dec::piece_total<VTPR>(acc[h][e]);
+        if (lane < NCV) {
             float *accw = (float *)&sm.ring[w][NSTAGE - 1][0];
 #pragma unroll
             for (int h = 0; h < G; ++h)
 #pragma unroll
-                for (int e = 0; e < E; ++e)
-                    accw[h * D + lane * E + e] = acc[h][e];
+                for (int e = 0; e < EV; ++e)
+                    accw[h * D + lane * EV + e] = acc[h][e];
         }
         if (lane < 16 && tr == 0 && lane_owner)
             sm.msum[w][1][lane_m] = ls;
@@ -963,24 +595,8 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(DecodeArgs a)
                 lo = (int)(item - x);
                 hi = lo + n_i - 1;
             } else {
-                const long long W = gridDim.x;
-                if (total_v > 0) {
-                    // work-groups whose (virtual) ranges hold the pair's real items;
-                    // every range holds at least one real item, so rank = index
-                    const long long first_v = vbase_i + (long long)g * (n_i + ALPHA) + ALPHA;
-                    const long long last_v = first_v + n_i - 1;
-                    lo = (int)(((first_v + 1) * W - 1) / total_v) + pair;
-                    hi = (int)(((last_v + 1) * W - 1) / total_v) + pair;
-                } else {
-                    const long long first_item = base_i + (long long)g * n_i;
-                    const long long last_item = first_item + n_i - 1;
-                    const long long k_first = ((first_item + 1) * W - 1) / total;
-                    const long long k_last = ((last_item + 1) * W - 1) / total;
-                    const long long r_first = k_first < k_first * total / W ? k_first : k_first * total / W;
-                    const long long r_last = k_last < k_last * total / W ? k_last : k_last * total / W;
-                    lo = (int)r_first + pair;
-                    hi = (int)r_last + pair;
-                }
+                dec::partial_slot_range(base_i + (long long)g * n_i, n_i, R,
+                                        vbase_i + (long long)g * (n_i + ALPHA) + ALPHA, pair, lo, hi);
             }
             wait_vm<0>();
             barrier_lds();
@@ -989,54 +605,9 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(DecodeArgs a)
                                                  __HIP_MEMORY_SCOPE_AGENT) == hi - lo;
             barrier_lds();
             if (sm.last) {
-                // merge slots lo..hi: thread = 4 consecutive d of one head; the
-                // (max, sum) and accumulator loads of up to 8 slots are issued
-                // together, so a typical merge costs one memory round trip
-                const int np = hi - lo + 1;
-                for (int e = 4 * tid; e < G * D; e += 4 * NT) {
-                    const int h = e / D;
-                    float M = -INFINITY, den = 0.f;
-                    float num[4] = {0.f, 0.f, 0.f, 0.f};
-                    for (int s0 = 0; s0 < np; s0 += 8) {
-                        f32x2 ml[8], ac[8][2];
-#pragma unroll
-                        for (int k = 0; k < 8; ++k) {
-                            if (s0 + k < np) {
-                                const int64_t sl = lo + s0 + k;
-                                ml[k] = coherent_load2(&a.ws_ml[(sl * G + h) * 2]);
-                                ac[k][0] = coherent_load2(&a.ws_acc[sl * G * D + e]);
-                                ac[k][1] = coherent_load2(&a.ws_acc[sl * G * D + e + 2]);
-                            } else {
-                                ml[k] = f32x2{-INFINITY, 0.f};
-                                ac[k][0] = ac[k][1] = f32x2{0.f, 0.f};
-                            }
-                        }
-                        float Mb = M;
-#pragma unroll
-                        for (int k = 0; k < 8; ++k)
-                            Mb = fmaxf(Mb, ml[k][0]);
-                        const float fo = M == -INFINITY ? 0.f : fast_exp2(M - Mb);
-                        den *= fo;
-#pragma unroll
-                        for (int j = 0; j < 4; ++j)
-                            num[j] *= fo;
-#pragma unroll
-                        for (int k = 0; k < 8; ++k) {
-                            const float f = ml[k][0] == -INFINITY ? 0.f : fast_exp2(ml[k][0] - Mb);
-                            den += f * ml[k][1];
-                            num[0] += f * ac[k][0][0];
-                            num[1] += f * ac[k][0][1];
-                            num[2] += f * ac[k][1][0];
-                            num[3] += f * ac[k][1][1];
-                        }
-                        M = Mb;
-                    }
-                    const float inv = a.v_scale / den;
-                    float *dst = a.out + ((int64_t)i * Hq + g * G) * D + e;
-#pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        dst[j] = num[j] * inv;
-                }
+                dec::merge_partials<G, D, NT, 8>(a.ws_ml, a.ws_acc, lo, hi - lo + 1,
+                                                 a.out + ((int64_t)i * Hq + g * G) * D, a.v_scale, tid,
+                                                 sm.merge);
                 if (tid == 0)
                     a.ws_count[pair] = 0;  // leave the counter at zero for the next call
             }

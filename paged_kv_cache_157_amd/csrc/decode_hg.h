@@ -1,14 +1,8 @@
 // decode_hg.h -- decode attention by KV-head groups: the variant used when a
 // model has at least two groups of four KV heads and G >= 2 (decode_hg4.hip
-// instantiates it; decode.hip holds the other kernel and the choice).
-//
-// What is computed ("Lecture 33" §2.3): for every sequence i and query head
-// h, out[i,h] = softmax(scale * q[i,h] K^T) V over the sequence's tokens,
-// whose K/V rows are read in place from scattered physical blocks through
-// the block table (logical block t/16, offset t%16, §2.2 walk-through).  The
-// pages name a streaming (online) softmax and no more; the recurrence used
-// here is the standard one: running maximum, running sum, rescaled
-// accumulator, followed by a log-sum-exp merge of partial results.
+// instantiates it; decode.hip holds the other kernel and the choice).  The
+// computation, the lane geometry, the start-up scan, the partial-record slots
+// and the merge are those of decode_common.h, shared with decode.hip.
 //
 // Work decomposition (MI355X: 256 CUs in 8 XCDs, wave64):
 //   * KV heads are taken HPG (four) at a time: a "head group".  The flat
@@ -44,143 +38,15 @@
 
 #include <type_traits>
 
-#include "pa_device.h"
-#include "pa_internal.h"
+#include "decode_common.h"
 
 namespace pa {
 namespace hg {
 
-typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
-
-template <int CDT, int D, int G>
-struct DecodeCfg {
-    static constexpr int EB = Storage<CDT>::bytes;
-    static constexpr int E = 16 / EB;            // cache elements per 16-byte chunk
-    static constexpr int NC = D / E;             // chunks in one token row of one head
-    static constexpr int LPT = G <= 4 ? 4 : 8;   // QK lanes per token
-    static constexpr int GP = G <= 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : 8;
-    static constexpr int CPL = NC / LPT;         // K chunks per lane and token
-    static constexpr int ROUNDS = LPT / 4;       // QK passes per 16-token block
-    static constexpr int TRN = 4 / ROUNDS;       // tokens per row per QK pass
-    // V is read in pieces of VB bytes (8 for fp8, so that a lane accumulates 8
-    // elements per head, as for bf16)
-    static constexpr int VB = CDT == DT_FP8 ? 8 : 16;
-    static constexpr int EV = VB / EB;           // cache elements per V piece
-    static constexpr int NCV = D / EV;           // V pieces in one token row of one head
-    static constexpr int VTPR = 16 / NCV;        // tokens per row per V pass
-    static constexpr int VPASS = 4 / VTPR;       // V passes per block
-    using VT = std::conditional_t<VB == 16, u32x4, u32x2>;
-    // q dwords per (head slot, K chunk): bf16 pairs matching the chunk, or fp32
-    static constexpr int QW = CDT == DT_FP8 ? 8 : 4;
-    static_assert(CPL >= 1 && NC <= 16 && NC >= 4, "unsupported chunk geometry");
-    static_assert(NCV <= 16 && NCV >= 4, "unsupported V geometry");
-    static_assert(G >= 1 && G <= 8, "GQA group must be 1..8");
-};
-
-// Token (0..15 within the block) held in "row" r at index k (0..3).  QK lanes
-// of row r handle exactly the tokens that the V lanes of row r accumulate, so
-// the running maximum of a row never has to leave it.
-template <int LPT>
-__host__ __device__ constexpr int row_token(int r, int k)
-{
-    if constexpr (LPT == 4)
-        return 4 * r + k;
-    else
-        return 2 * r + (k & 1) + 8 * (k >> 1);
-}
-
-// The tokens of a lane's later QK rounds (V passes) lie a fixed number of
-// token rows after those of its first: row_token(r, k0 + d) = row_token(r, k0)
-// + row_token(0, d) for every row r and first index k0 the geometry uses, so
-// one lane offset plus a scalar offset per round (pass) addresses them all.
-template <int LPT, int STEP, int NSTEP, int K0S>
-constexpr bool rows_shift_evenly()
-{
-    for (int r = 0; r < 4; ++r)
-        for (int k0 = 0; k0 < K0S; ++k0)
-            for (int n = 0; n < NSTEP; ++n)
-                if (row_token<LPT>(r, k0 + n * STEP) != row_token<LPT>(r, k0) + row_token<LPT>(0, n * STEP))
-                    return false;
-    return true;
-}
-
-// Reduce-scatter of GP partial sums over the LPT lanes of one token.  On
-// entry slot s of a lane holds the partial sum of head (s ^ mask); on exit
-// x[0] holds the complete sum of head `mask`.
-template <int LPT, int GP>
-__device__ __forceinline__ float reduce_scatter(float (&x)[GP])
-{
-    if constexpr (LPT == 8) {
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-            x[k] += dpp<DPP_HALF_MIRROR>(x[k + 4]);
-#pragma unroll
-        for (int k = 0; k < 2; ++k)
-            x[k] += dpp<DPP_QP_X1>(x[k + 2]);
-        x[0] += dpp<DPP_QP_X2>(x[1]);
-    } else if constexpr (GP == 4) {
-#pragma unroll
-        for (int k = 0; k < 2; ++k)
-            x[k] += dpp<DPP_QP_X1>(x[k + 2]);
-        x[0] += dpp<DPP_QP_X2>(x[1]);
-    } else if constexpr (GP == 2) {
-        x[0] += dpp<DPP_QP_X1>(x[1]);
-        x[0] += dpp<DPP_QP_X2>(x[0]);
-    } else {
-        x[0] += dpp<DPP_QP_X1>(x[0]);
-        x[0] += dpp<DPP_QP_X2>(x[0]);
-    }
-    return x[0];
-}
-
-// Head handled by a lane after reduce_scatter, and whether the lane is the
-// single owner of that (token, head) value (others hold copies).
-template <int LPT, int GP>
-__device__ __forceinline__ int head_mask(int lane)
-{
-    const int b0 = lane & 1, b1 = (lane >> 1) & 1, b2 = (lane >> 2) & 1;
-    if constexpr (LPT == 8)
-        return 4 * b2 + 2 * (b0 ^ b2) + (b1 ^ b2);
-    else if constexpr (GP == 4)
-        return 2 * b0 + b1;
-    else if constexpr (GP == 2)
-        return b0;
-    else
-        return 0;
-}
-template <int LPT, int GP>
-__device__ __forceinline__ bool mask_owner(int lane)
-{
-    if constexpr (LPT == 8 || GP == 4)
-        return true;
-    else if constexpr (GP == 2)
-        return ((lane >> 1) & 1) == 0;
-    else
-        return (lane & 3) == 0;
-}
-
-// Sum over the 64 lanes of a wave.
-__device__ __forceinline__ long long wave_sum64(long long v)
-{
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1)
-        v += __shfl_xor(v, d);
-    return v;
-}
-
-// Sum of a value over the 64 lanes that share a "column" pattern: lanes that
-// differ only in the row (bits 4-5) and in the bits selected by the pattern.
-// gfx950's lane swaps exchange the wave halves (rows 0-1 <-> 2-3) and
-// neighbouring rows in registers: swapping a value with itself leaves
-// {v(l), v(l ^ 32)} (then {v(l), v(l ^ 16)}) in the two results of every
-// lane l.
-__device__ __forceinline__ float sum_rows(float v)
-{
-    const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    v = __uint_as_float(h[0]) + __uint_as_float(h[1]);
-    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
+using dec::u32x2;
+using dec::row_token;
+using dec::rows_shift_evenly;
+using dec::wait_vm;
 
 // Partial results whose hand-over (arrival count, and the merge by the last
 // contributor) is still pending in a work-group.  Balanced split: at most two
@@ -199,35 +65,20 @@ struct DecodeSmem {
     float bmax[HPG][4][8];     // row maxima (rescale path)
     float lsum[HPG][8];        // a wave's softmax sums at a segment end
     float mref[HPG][8];        // a wave's running (reference) maximum per head
-    long long total;  // item count of the call (start-up scan)
-    int seg_i, seg_L;
-    long long seg_base;
+    dec::Range range;  // this work-group's range (start-up scan)
     // pending hand-overs: first slot, slot count, counter index, output row
     int def_lo[kDecodeDeferred], def_np[kDecodeDeferred], def_pair[kDecodeDeferred];
     long long def_out[kDecodeDeferred];
     int def_last[kDecodeDeferred];
-    // merge of one (sequence, head group): per query head of the group, the
-    // running maximum and denominator, and the scale factors of a batch of 8
-    // partials (and of the running sums)
-    float mM[32], mden[32], mfo[32], mf[8][32];
+    dec::MergeLds<HPG * G, 8> merge;  // merge of one (sequence, head group)
 };
 
-// Word 3 of a raw buffer descriptor (32-bit data format, no swizzle).
-constexpr int kBufferRsrcWord3 = 0x00020000;
-// Cache policy of a device-coherent (L2-bypassing) buffer load: sc1.
-constexpr int kBufferCoherent = 16;
-
-// s_waitcnt vmcnt(N)
-template <int N>
-__device__ __forceinline__ void wait_vm()
-{
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
+using dec::kBufferRsrcWord3;
 
 template <int CDT, int D, int G, int HPG>
 __global__ __launch_bounds__(64 * HPG, 2) void decode_hg_kernel(DecodeArgs a)
 {
-    using C = DecodeCfg<CDT, D, G>;
+    using C = dec::DecodeCfg<CDT, D, G, CDT == DT_FP8 ? 8 : 16>;
     using SM = DecodeSmem<CDT, D, G, HPG>;
     constexpr int WAVES = HPG;
     constexpr int NT = 64 * WAVES;
@@ -250,77 +101,29 @@ __global__ __launch_bounds__(64 * HPG, 2) void decode_hg_kernel(DecodeArgs a)
         return (tab[u >> ts] << ts) + (u & ((1 << ts) - 1));
     };
 
-    auto items_of = [&](int L) -> int {
-        L = L < 0 ? 0 : L;
-        int nb = (L + 15) >> 4;
-        nb = nb > maxU ? maxU : nb;
-        return PB > 0 ? (nb + PB - 1) / PB : nb;
-    };
-
-    // ---- total item count and the sequence holding this work-group's first
-    // item: wave 0 scans the lengths 64 at a time with shuffles (no work-group
-    // barrier inside); the other waves wait at the barrier below.
+    // ---- this work-group's range of items (plain equal split); wave 0 scans,
+    // the others wait at the barrier below
     if (w == 0) {
-        const int l0 = lane < S ? a.context_lens[lane] : 0;
-        const long long v0 = items_of(l0);
-        long long cnt = wave_sum64(v0);
-        for (int base = 64; base < S; base += 64) {
-            const int s2 = base + lane;
-            cnt += wave_sum64(s2 < S ? (long long)items_of(a.context_lens[s2]) : 0);
-        }
-        const long long tot = cnt * NHG;
-        const long long x0 = tot * blockIdx.x / gridDim.x;
-        int found = -1, fL = 0;
-        long long fbase = 0, carry = 0;
-        for (int base = 0; base < S; base += 64) {
-            const int s2 = base + lane;
-            const int l = base == 0 ? l0 : s2 < S ? a.context_lens[s2] : 0;
-            const long long v = (long long)items_of(l) * NHG;
-            long long incl = v;
-#pragma unroll
-            for (int d = 1; d < 64; d <<= 1) {
-                const long long t = __shfl_up(incl, d);
-                if (lane >= d)
-                    incl += t;
-            }
-            const long long excl = incl - v;
-            const unsigned long long m =
-                __builtin_amdgcn_ballot_w64(v > 0 && carry + excl <= x0 && x0 < carry + incl);
-            if (m) {
-                const int l2 = __builtin_ctzll(m);
-                found = base + l2;
-                fbase = carry + __shfl(excl, l2);
-                fL = __shfl(l, l2);
-                break;
-            }
-            carry += __shfl(incl, 63);
-        }
-        if (lane == 0) {
-            sm.total = tot;
-            sm.seg_i = found;
-            sm.seg_L = fL;
-            sm.seg_base = fbase;
-        }
+        const dec::Range R = dec::startup_scan<0>(a.context_lens, S, NHG, maxU, PB, lane);
+        if (lane == 0)
+            sm.range = R;
     }
     __syncthreads();
-    const long long total = uniform64(sm.total);
-    if (blockIdx.x == 0) {  // sequences with no tokens get a zero output row
-        for (int i = tid; i < S; i += NT)
-            if (a.context_lens[i] <= 0)
-                for (int e = 0; e < Hq * D; ++e)
-                    a.out[(int64_t)i * Hq * D + e] = 0.f;
-    }
-    const long long a0 = total * blockIdx.x / gridDim.x;
-    const long long a1 = total * (blockIdx.x + 1) / gridDim.x;
+    dec::Range R;
+    R.total = uniform64(sm.range.total);
+    R.total_v = 0;
+    dec::zero_empty_rows<D, NT>(a.context_lens, a.out, S, Hq, tid);
+    const long long a0 = uniform64(sm.range.r0);
+    const long long a1 = uniform64(sm.range.r1);
     if (a0 >= a1)
         return;
-    int i = uniform(sm.seg_i);
+    int i = uniform(sm.range.seq);
     if (i < 0)  // unreachable while a0 < total; keeps every index in range
         return;
-    long long base_i = uniform64(sm.seg_base);  // first item index of sequence i
+    long long base_i = uniform64(sm.range.base);  // first item index of sequence i
     long long item = a0;
-    const int lane_m = head_mask<LPT, GP>(lane);
-    const bool lane_owner = mask_owner<LPT, GP>(lane) && lane_m < G;
+    const int lane_m = dec::head_mask<LPT, GP>(lane);
+    const bool lane_owner = dec::mask_owner<LPT, GP>(lane) && lane_m < G;
     const int row = lane >> 4;
 
     // QK lane geometry
@@ -341,7 +144,7 @@ __global__ __launch_bounds__(64 * HPG, 2) void decode_hg_kernel(DecodeArgs a)
     static_assert(rows_shift_evenly<LPT, C::TRN, ROUNDS, C::TRN>(), "K rounds");
     static_assert(rows_shift_evenly<LPT, VTPR, VPASS, VTPR>(), "V passes");
     const int koff = (int)(row_token<LPT>(row, tr) * tok_bytes) + gl * 16;
-    const int voff = (int)(row_token<LPT>(row, vh) * tok_bytes) + vc * C::VB;
+    const int voff = (int)(row_token<LPT>(row, vh) * tok_bytes) + vc * C::VPB;
 
     const auto lens_s = scalar_view(a.context_lens);
     constexpr int QEB = CDT == DT_F32 ? 4 : 2;  // bytes per q element
@@ -359,11 +162,11 @@ __global__ __launch_bounds__(64 * HPG, 2) void decode_hg_kernel(DecodeArgs a)
     };
     auto describe = [&](long long it, int &si, long long sbase, int L) -> Seg {
         Seg d;
-        int n = items_of(L);
+        int n = dec::items_of(L, maxU, PB);
         while (n == 0) {  // cannot happen for the first segment; skip empties
             ++si;
             L = lens_s[si];
-            n = items_of(L);
+            n = dec::items_of(L, maxU, PB);
         }
         d.L = uniform(L > maxU * 16 ? maxU * 16 : L);
         d.n_i = uniform(n);
@@ -381,12 +184,7 @@ __global__ __launch_bounds__(64 * HPG, 2) void decode_hg_kernel(DecodeArgs a)
             d.seg_items = (int)((long long)(d.n_i - d.x) < left ? (d.n_i - d.x) : left);
             d.b0 = d.x;
             d.b1 = d.x + d.seg_items;
-            // rank of this work-group among those with a non-empty range: with at
-            // least as many items as work-groups every range is non-empty (rank =
-            // blockIdx.x); with fewer, each non-empty range holds one item (rank =
-            // a0).  Ranks keep the partial slots of one (sequence, head group)
-            // contiguous.
-            d.slot = (int)(a0 < (long long)blockIdx.x ? a0 : (long long)blockIdx.x) + si * NHG + d.hg;
+            d.slot = dec::partial_slot(a0, si * NHG + d.hg);
         }
         d.b0 = uniform(d.b0);
         d.b1 = uniform(d.b1);
@@ -443,7 +241,7 @@ __global__ __launch_bounds__(64 * HPG, 2) void decode_hg_kernel(DecodeArgs a)
 #pragma unroll
         for (int v = 0; v < VPASS; ++v) {
             const int vrow = (int)(row_token<LPT>(0, v * VTPR) * tok_bytes);
-            if constexpr (C::VB == 16)
+            if constexpr (C::VPB == 16)
                 vr[v] = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, vrow, 0);
             else
                 vr[v] = __builtin_amdgcn_raw_buffer_load_b64(rs, voff, vrow, 0);
@@ -453,31 +251,7 @@ __global__ __launch_bounds__(64 * HPG, 2) void decode_hg_kernel(DecodeArgs a)
         return (const char *)cache + (int64_t)(hg * HPG + w) * D * C::EB;
     };
 
-    // Issue priority follows this wave's remaining work (3 at the start, 0 near
-    // the end): when two work-groups share a CU, the one that has fallen behind
-    // gets the instruction slots, instead of the older one by default, so both
-    // finish together.  The persistent grid fills every CU's first slots with
-    // the first half of the work-groups before the rest; the later ones lower
-    // their priority half a step later, which cancels the age tie-break at
-    // equal progress.  Only the order of issue changes, never the arithmetic.
-    const int exp_w = (int)(a1 - a0);  // blocks of this wave
-    const int ew = exp_w > 0 ? exp_w : 1;
-    const int lag = blockIdx.x >= gridDim.x / 2 ? ew / 2 : 0;
-    int done_w = 0, cur_prio = -1;
-    auto update_priority = [&]() {
-        const int pr = 3 - min(3, max(0, 4 * done_w - lag) / ew);
-        if (pr != cur_prio) {
-            cur_prio = pr;
-            if (pr == 3)
-                __builtin_amdgcn_s_setprio(3);
-            else if (pr == 2)
-                __builtin_amdgcn_s_setprio(2);
-            else if (pr == 1)
-                __builtin_amdgcn_s_setprio(1);
-            else
-                __builtin_amdgcn_s_setprio(0);
-        }
-    };
+    dec::IssuePriority prio((int)(a1 - a0));  // blocks of this wave
 
     // ---- hand-over of partial results.  The partial records of one
     // (sequence, head group) are the contiguous slot range [lo, lo + np), each
@@ -502,97 +276,11 @@ __global__ __launch_bounds__(64 * HPG, 2) void decode_hg_kernel(DecodeArgs a)
                                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
                                sm.def_np[tid] - 1;
         __syncthreads();
-        static_assert(HG <= 32, "merge scratch holds 32 query heads");
-        constexpr int KC = (HG * D + 4 * NT - 1) / (4 * NT);  // 4-column chunks per thread
         for (int k = 0; k < ndef; ++k) {
             if (!sm.def_last[k])
                 continue;
-            const int lo = sm.def_lo[k], np = sm.def_np[k];
-            float *out_row = a.out + sm.def_out[k];
-            // the np records of this (sequence, head group); loads past them read zero
-            const auto rs = __builtin_amdgcn_make_buffer_rsrc(
-                (void *)(a.ws_acc + (int64_t)lo * HG * D), (short)0, np * HG * D * 4, kBufferRsrcWord3);
-            float num[KC][4];
-#pragma unroll
-            for (int kc = 0; kc < KC; ++kc)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    num[kc][j] = 0.f;
-            if (tid < HG) {
-                sm.mM[tid] = -INFINITY;
-                sm.mden[tid] = 0.f;
-            }
-            __syncthreads();
-            // batches of MB partials: every thread issues the accumulator loads of
-            // its columns, the threads that own a head load the (max, sum)
-            // pairs and publish the scale factors, then all combine: one memory
-            // round trip per batch
-            for (int s0 = 0; s0 < np; s0 += MB) {
-                u32x4 ac[MB][KC];
-#pragma unroll
-                for (int k2 = 0; k2 < MB; ++k2)
-#pragma unroll
-                    for (int kc = 0; kc < KC; ++kc) {
-                        const int e = 4 * tid + kc * 4 * NT;
-                        ac[k2][kc] = e < HG * D ? __builtin_amdgcn_raw_buffer_load_b128(
-                                                      rs, ((s0 + k2) * HG * D + e) * 4, 0, kBufferCoherent)
-                                                : u32x4{0u, 0u, 0u, 0u};
-                    }
-                if (tid < HG) {
-                    f32x2 ml[MB];
-#pragma unroll
-                    for (int k2 = 0; k2 < MB; ++k2)
-                        ml[k2] = s0 + k2 < np
-                                     ? coherent_load2(&a.ws_ml[((int64_t)(lo + s0 + k2) * HG + tid) * 2])
-                                     : f32x2{-INFINITY, 0.f};
-                    const float M = sm.mM[tid];
-                    float Mb = M;
-#pragma unroll
-                    for (int k2 = 0; k2 < MB; ++k2)
-                        Mb = fmaxf(Mb, ml[k2][0]);
-                    const float fo = M == -INFINITY ? 0.f : fast_exp2(M - Mb);
-                    float den = sm.mden[tid] * fo;
-#pragma unroll
-                    for (int k2 = 0; k2 < MB; ++k2) {
-                        const float f = ml[k2][0] == -INFINITY ? 0.f : fast_exp2(ml[k2][0] - Mb);
-                        den += f * ml[k2][1];
-                        sm.mf[k2][tid] = f;
-                    }
-                    sm.mfo[tid] = fo;
-                    sm.mM[tid] = Mb;
-                    sm.mden[tid] = den;
-                }
-                __syncthreads();
-#pragma unroll
-                for (int kc = 0; kc < KC; ++kc) {
-                    const int e = 4 * tid + kc * 4 * NT;
-                    if (e < HG * D) {
-                        const int h = e / D;
-                        const float fo = sm.mfo[h];
-#pragma unroll
-                        for (int j = 0; j < 4; ++j)
-                            num[kc][j] *= fo;
-#pragma unroll
-                        for (int k2 = 0; k2 < MB; ++k2) {
-                            const float f = sm.mf[k2][h];
-#pragma unroll
-                            for (int j = 0; j < 4; ++j)
-                                num[kc][j] = fmaf(f, __uint_as_float(ac[k2][kc][j]), num[kc][j]);
-                        }
-                    }
-                }
-                __syncthreads();  // the scale factors of the next batch go to the same place
-            }
-#pragma unroll
-            for (int kc = 0; kc < KC; ++kc) {
-                const int e = 4 * tid + kc * 4 * NT;
-                if (e < HG * D) {
-                    const float inv = a.v_scale / sm.mden[e / D];
-#pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        out_row[e + j] = num[kc][j] * inv;
-                }
-            }
+            dec::merge_partials<HG, D, NT, MB>(a.ws_ml, a.ws_acc, sm.def_lo[k], sm.def_np[k],
+                                               a.out + sm.def_out[k], a.v_scale, tid, sm.merge);
             if (tid == 0)
                 a.ws_count[sm.def_pair[k]] = 0;  // leave the counter at zero for the next call
         }
@@ -604,7 +292,7 @@ __global__ __launch_bounds__(64 * HPG, 2) void decode_hg_kernel(DecodeArgs a)
     // a load also waits for every load issued before it), then its first two
     // blocks into slots 0 and 1 (the segment's first block again in slot 1 when
     // it has only one: a null block, see below)
-    Seg sg = describe(item, i, base_i, uniform(sm.seg_L));
+    Seg sg = describe(item, i, base_i, lens_s[i]);
     load_q(i, sg.hg * HPG + w);
     store_q();
     {
@@ -675,8 +363,7 @@ __global__ __launch_bounds__(64 * HPG, 2) void decode_hg_kernel(DecodeArgs a)
 
         auto step = [&](int b, u32x4 (&kr)[ROUNDS][CPL], VT (&vr)[VPASS], int pb2,
                         const char *kb2, const char *vb2) {
-            update_priority();
-            ++done_w;
+            prio.step();
 
             // -- scores of this lane's token(s) for head lane_m ------------
             const int tbase = b * 16;
@@ -702,30 +389,14 @@ __global__ __launch_bounds__(64 * HPG, 2) void decode_hg_kernel(DecodeArgs a)
                             qc[4 * k + e] = u[e];
                     }
 #pragma unroll
-                    for (int j = 0; j < ROUNDS; ++j) {
-                        const u32x4 kc = kr[j][c];
-                        if constexpr (CDT == DT_BF16) {
-#pragma unroll
-                            for (int p = 0; p < 4; ++p)
-                                xs[j][s] = dot2_bf16(qc[p], kc[p], xs[j][s]);
-                        } else if constexpr (CDT == DT_FP8) {
-#pragma unroll
-                            for (int p = 0; p < 4; ++p) {
-                                xs[j][s] = dot2_bf16(qc[2 * p], fp8x2_to_bf16x2<false>(kc[p]), xs[j][s]);
-                                xs[j][s] = dot2_bf16(qc[2 * p + 1], fp8x2_to_bf16x2<true>(kc[p]), xs[j][s]);
-                            }
-                        } else {
-#pragma unroll
-                            for (int p = 0; p < 4; ++p)
-                                xs[j][s] = fmaf(__uint_as_float(qc[p]), __uint_as_float(kc[p]), xs[j][s]);
-                        }
-                    }
+                    for (int j = 0; j < ROUNDS; ++j)
+                        xs[j][s] = dec::dot_chunk<CDT, QW>(qc, kr[j][c], xs[j][s]);
                 }
             }
             float sc[ROUNDS];
 #pragma unroll
             for (int j = 0; j < ROUNDS; ++j) {
-                const float s2 = reduce_scatter<LPT, GP>(xs[j]) * a.qk_scale;
+                const float s2 = dec::reduce_scatter<LPT, GP>(xs[j]) * a.qk_scale;
                 const int tt = tbase + row_token<LPT>(row, tr + j * C::TRN);
                 sc[j] = tt < L ? s2 : -INFINITY;
             }
@@ -799,27 +470,7 @@ __global__ __launch_bounds__(64 * HPG, 2) void decode_hg_kernel(DecodeArgs a)
                 for (int h = 0; h < G; ++h)
                     pr[h] = sm.p[w][tk][h];
                 float ve[EV];
-                if constexpr (CDT == DT_BF16) {
-#pragma unroll
-                    for (int k = 0; k < 4; ++k) {
-                        ve[2 * k] = bf16_lo(vv[k]);
-                        ve[2 * k + 1] = bf16_hi(vv[k]);
-                    }
-                } else if constexpr (CDT == DT_FP8) {
-#pragma unroll
-                    for (int k = 0; k < 2; ++k) {
-                        const f32x2 lo = fp8x2_to_f32x2<false>(vv[k]);
-                        const f32x2 hi = fp8x2_to_f32x2<true>(vv[k]);
-                        ve[4 * k] = lo[0];
-                        ve[4 * k + 1] = lo[1];
-                        ve[4 * k + 2] = hi[0];
-                        ve[4 * k + 3] = hi[1];
-                    }
-                } else {
-#pragma unroll
-                    for (int k = 0; k < 4; ++k)
-                        ve[k] = __uint_as_float(vv[k]);
-                }
+                dec::widen_v<CDT, EV>(vv, ve);
 #pragma unroll
                 for (int h = 0; h < G; ++h)
 #pragma unroll
@@ -857,24 +508,12 @@ __global__ __launch_bounds__(64 * HPG, 2) void decode_hg_kernel(DecodeArgs a)
 
         // ---- this wave's totals for its head -> output or partial -----------
         // sum over rows and over the lanes of a row that hold other tokens
-        float ls = lane_owner ? lsum : 0.f;
-        ls = sum_rows(ls);
-        if constexpr (LPT == 4)
-            ls += dpp<DPP_ROW_ROR4>(ls);
-        ls += dpp<DPP_ROW_ROR8>(ls);
+        const float ls = dec::token_total<LPT>(lane_owner ? lsum : 0.f);
 #pragma unroll
         for (int h = 0; h < G; ++h)
 #pragma unroll
-            for (int e = 0; e < EV; ++e) {
-                float t = sum_rows(acc[h][e]);
-                if constexpr (VTPR == 2)
-                    t += dpp<DPP_ROW_ROR8>(t);
-                if constexpr (VTPR == 4) {
-                    t += dpp<DPP_ROW_ROR4>(t);
-                    t += dpp<DPP_ROW_ROR8>(t);
-                }
-                acc[h][e] = t;
-            }
+            for (int e = 0; e < EV; ++e)
+                acc[h][e] = dec::piece_total<VTPR>(acc[h][e]);
         if (lane < 16 && tr == 0 && lane_owner)
             sm.lsum[w][lane_m] = ls;
         __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
@@ -914,15 +553,7 @@ __global__ __launch_bounds__(64 * HPG, 2) void decode_hg_kernel(DecodeArgs a)
                 lo = (int)(item - x);
                 hi = lo + n_i - 1;
             } else {
-                const long long W = gridDim.x;
-                const long long first_item = base_i + (long long)hg * n_i;
-                const long long last_item = first_item + n_i - 1;
-                const long long k_first = ((first_item + 1) * W - 1) / total;
-                const long long k_last = ((last_item + 1) * W - 1) / total;
-                const long long r_first = k_first < k_first * total / W ? k_first : k_first * total / W;
-                const long long r_last = k_last < k_last * total / W ? k_last : k_last * total / W;
-                lo = (int)r_first + pair;
-                hi = (int)r_last + pair;
+                dec::partial_slot_range(base_i + (long long)hg * n_i, n_i, R, 0, pair, lo, hi);
             }
             if (tid == 0) {
                 sm.def_lo[ndef] = lo;

@@ -40,7 +40,7 @@ TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
 
 def decode_source_hash() -> str:
     h = hashlib.sha256()
-    for f in ("decode.hip", "decode_hg.h", "decode_hg4.hip", "pa_device.h"):
+    for f in ("decode.hip", "decode_common.h", "decode_hg.h", "decode_hg4.hip", "pa_device.h"):
         p = os.path.join(HERE, "csrc", f)
         if os.path.exists(p):
             h.update(open(p, "rb").read())
