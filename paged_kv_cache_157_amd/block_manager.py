@@ -36,7 +36,7 @@ from typing import Dict, Iterable, List, Optional, Sequence, Tuple
 
 import numpy as np
 
-BLOCK_SIZE = 16  # tokens per KV block ([L33] §2.2; [VM] §1)
+BLOCK_SIZE = 16  # default tokens per KV block ([L33] §2.2; [VM] §1); a pool may use 8, 32 or 64
 
 
 class PoolExhausted(RuntimeError):
@@ -80,10 +80,13 @@ class BlockPool:
     tail, and a prefix hit unlinks a cached block from anywhere, each O(1).
     """
 
-    def __init__(self, num_blocks: int, seed: Optional[int] = None):
+    def __init__(self, num_blocks: int, seed: Optional[int] = None, block_size: int = BLOCK_SIZE):
         if num_blocks <= 0:
             raise ValueError("num_blocks must be positive")
+        if block_size not in (8, 16, 32, 64):
+            raise ValueError("block_size must be 8, 16, 32 or 64 tokens")
         self.num_blocks = int(num_blocks)
+        self.block_size = int(block_size)  # tokens per block ([L33] §2.2, appendix Q3)
         order = np.arange(self.num_blocks)
         if seed is not None:
             order = np.random.Generator(np.random.PCG64(seed)).permutation(self.num_blocks)
@@ -227,11 +230,15 @@ class SeqTable:
     # the token ids, while every token's id is known (prefix caching)
     token_ids: Optional[List[int]] = None
 
+    @property
+    def block_size(self) -> int:
+        return self.pool.block_size
+
     @classmethod
     def allocate(cls, pool: BlockPool, num_tokens: int) -> "SeqTable":
         """Table for a fresh sequence already holding ``num_tokens`` tokens."""
         t = cls(pool)
-        t.blocks = pool.allocate(-(-num_tokens // BLOCK_SIZE))
+        t.blocks = pool.allocate(-(-num_tokens // pool.block_size))
         t.num_tokens = num_tokens
         return t
 
@@ -243,15 +250,17 @@ class SeqTable:
         The last shared block may be partly filled (a fork, [L33] §2.4); the
         first write into it then goes through copy-on-write.
         """
-        if num_tokens <= (len(prefix) - 1) * BLOCK_SIZE:
+        B = pool.block_size
+        if num_tokens <= (len(prefix) - 1) * B:
             raise ValueError("a sequence must reach into every block it shares")
-        extra = max(0, -(-num_tokens // BLOCK_SIZE) - len(prefix))
+        extra = max(0, -(-num_tokens // B) - len(prefix))
         own = pool.allocate(extra)
         pool.share(prefix)
         return cls(pool, list(prefix) + own, num_tokens)
 
     @classmethod
-    def allocate_cached(cls, pool: BlockPool, token_ids: Sequence[int]) -> Tuple["SeqTable", int]:
+    def allocate_cached(cls, pool: BlockPool, token_ids: Sequence[int],
+                        reserve: int = 0) -> Tuple["SeqTable", int]:
         """Table for a new request with prompt ``token_ids``, reusing cached
         blocks for its longest cached prefix of full blocks ([VM] §3.4;
         [L33] §6.2).  Returns ``(table, hit_tokens)``: the first hit_tokens
@@ -259,12 +268,13 @@ class SeqTable:
         never covers the whole prompt: at least its last token is computed
         (the step needs an output for it), so a fully cached prompt gives
         back its last full block.  Raises PoolExhausted, with no block taken,
-        when the rest does not fit."""
+        when the rest does not fit next to ``reserve`` blocks kept free."""
         n = len(token_ids)
-        full = n // BLOCK_SIZE
+        B = pool.block_size
+        full = n // B
         hashes, parent = [], None
         for j in range(full):
-            parent = block_hash(parent, token_ids[j * BLOCK_SIZE:(j + 1) * BLOCK_SIZE])
+            parent = block_hash(parent, token_ids[j * B:(j + 1) * B])
             hashes.append(parent)
         hit = []
         for h in hashes:
@@ -272,15 +282,16 @@ class SeqTable:
             if b is None:
                 break
             hit.append(b)
-        if hit and len(hit) * BLOCK_SIZE >= n:
+        if hit and len(hit) * B >= n:
             hit.pop()
-        need = -(-n // BLOCK_SIZE) - len(hit)
+        need = -(-n // B) - len(hit)
         queued = sum(1 for b in hit if pool.ref_cnt(b) == 0)  # leave the queue on the hit
-        if need > pool.num_free - queued:
-            raise PoolExhausted(f"need {need} blocks, {pool.num_free - queued} free after the hit")
+        if need > pool.num_free - queued - reserve:
+            raise PoolExhausted(f"need {need} blocks, {pool.num_free - queued} free after the hit, "
+                                f"{reserve} kept")
         pool.touch(hit)
         t = cls(pool, hit + pool.allocate(need), n, hashes, [int(x) for x in token_ids])
-        return t, len(hit) * BLOCK_SIZE
+        return t, len(hit) * B
 
     def cache_full_blocks(self) -> None:
         """Register this table's full blocks of known tokens as cached prefix
@@ -289,9 +300,9 @@ class SeqTable:
             self.pool.cache_block(b, h)
 
     def slot(self, position: int) -> int:
-        if not 0 <= position < len(self.blocks) * BLOCK_SIZE:
+        if not 0 <= position < len(self.blocks) * self.block_size:
             raise IndexError(f"position {position} is not backed by a block")
-        return slot_of(self.blocks, position)
+        return slot_of(self.blocks, position, self.block_size)
 
     def append_token(self, token_id: Optional[int] = None) -> Tuple[int, Optional[Tuple[int, int]]]:
         """Reserve the slot of the next token.
@@ -307,11 +318,12 @@ class SeqTable:
         caller must perform on the device before writing; otherwise None.
         """
         pos = self.num_tokens
+        B = self.block_size
         cow = None
-        if pos == len(self.blocks) * BLOCK_SIZE:
+        if pos == len(self.blocks) * B:
             self.blocks += self.pool.allocate(1)
         else:
-            lb = pos // BLOCK_SIZE
+            lb = pos // B
             src = self.blocks[lb]
             if self.pool.ref_cnt(src) > 1:
                 dst = self.pool.allocate(1)[0]
@@ -324,9 +336,9 @@ class SeqTable:
                 self.token_ids = None
             else:
                 self.token_ids.append(int(token_id))
-                if self.num_tokens % BLOCK_SIZE == 0 and len(self.hashes) == self.num_tokens // BLOCK_SIZE - 1:
+                if self.num_tokens % B == 0 and len(self.hashes) == self.num_tokens // B - 1:
                     parent = self.hashes[-1] if self.hashes else None
-                    self.hashes.append(block_hash(parent, self.token_ids[-BLOCK_SIZE:]))
+                    self.hashes.append(block_hash(parent, self.token_ids[-B:]))
         return self.slot(pos), cow
 
     def extend(self, n: int) -> Tuple[List[int], List[Tuple[int, int]]]:
@@ -341,12 +353,13 @@ class SeqTable:
         first, cow = self.append_token()
         slots = [first]
         pos = self.num_tokens
-        room = len(self.blocks) * BLOCK_SIZE - pos
+        B = self.block_size
+        room = len(self.blocks) * B - pos
         rest = n - 1
         if rest > room:
-            self.blocks += self.pool.allocate(-(-(rest - room) // BLOCK_SIZE))
+            self.blocks += self.pool.allocate(-(-(rest - room) // B))
         for p in range(pos, pos + rest):
-            slots.append(slot_of(self.blocks, p))
+            slots.append(slot_of(self.blocks, p, B))
         self.num_tokens = pos + rest
         return slots, [cow] if cow is not None else []
 
@@ -361,7 +374,7 @@ class SeqTable:
 
     def waste(self) -> int:
         """Reserved but unused token slots (always < one block)."""
-        return len(self.blocks) * BLOCK_SIZE - self.num_tokens
+        return len(self.blocks) * self.block_size - self.num_tokens
 
 
 def swap_out(table: SeqTable, host: BlockPool) -> List[Tuple[int, int]]:
@@ -370,6 +383,8 @@ def swap_out(table: SeqTable, host: BlockPool) -> List[Tuple[int, int]]:
     another table shares stays on the device for it), and the table now
     points into the host pool.  Returns the (device, host) block copies to
     run before the freed device blocks are reused."""
+    if host.block_size != table.pool.block_size:
+        raise ValueError("device and host pools must use the same block size")
     hb = host.allocate(len(table.blocks))
     pairs = list(zip(table.blocks, hb))
     table.pool.free(table.blocks)

@@ -11,11 +11,18 @@ requests return their blocks.  Request lengths, q rows and new K/V rows are
 synthetic and seeded: lengths stand in for end-of-sequence, N(0,1) rows for
 the projections of a model.
 
+With a system prompt configured, requests carry token ids and are admitted
+through the prefix cache: a request whose prompt starts with cached full
+blocks reuses them and prefills only the rest.  The block size of the pools
+is a parameter (8, 16, 32 or 64 tokens).
+
 Sources, cited by page title and section: "Lecture 33: KV Cache memory
 management -- PagedAttention, Continuous Batching and Chunked Prefill" §3.2
 (iteration-level scheduling), §4.2-4.4 (chunked prefill under one token
-budget), §5.2 (preemption by swapping); "PagedAttention: managing the KV cache like virtual memory" §3.3
-(blocks taken as sequences grow, returned as they end).
+budget), §5.2 (preemption by swapping), §6.1-6.3 (prefix caching), §2.2 and
+appendix Q3 (block size); "PagedAttention: managing the KV cache like virtual
+memory" §3.3 (blocks taken as sequences grow, returned as they end), §3.4
+(prefix sharing by block hashes).
 """
 from __future__ import annotations
 
@@ -28,7 +35,7 @@ import numpy as np
 import torch
 
 from . import binding
-from .block_manager import BLOCK_SIZE, BlockPool
+from .block_manager import BlockPool
 from .scheduler import Scheduler, StepPlan, synthetic_requests
 
 _TORCH = {"bf16": torch.bfloat16, "fp8": torch.float8_e4m3fn}
@@ -50,6 +57,10 @@ class ReplayConfig:
     kv_scale: float = 1.0
     decode_reserve: bool = True  # False: admit greedily, preempt by swapping
     host_blocks: int = 0         # blocks of the pinned host pools (swap space)
+    block_size: int = 16         # tokens per block: 8, 16, 32 or 64
+    system_prompt: int = 0       # > 0: requests carry token ids, and a fraction
+    share: float = 0.0           #   `share` of them starts with one system prompt
+                                 #   of this many tokens (prefix caching)
 
     @property
     def scale(self) -> float:
@@ -57,7 +68,7 @@ class ReplayConfig:
 
     @property
     def width(self) -> int:
-        return -(-(self.prompt[1] + self.output[1]) // BLOCK_SIZE)
+        return -(-(self.system_prompt + self.prompt[1] + self.output[1]) // self.block_size)
 
     @property
     def kv_bytes_per_token(self) -> int:
@@ -69,6 +80,12 @@ REPLAYS = {
     "replay_qwen7b": ReplayConfig("replay_qwen7b", 28, 4, 128, "bf16", num_blocks=40000,
                                   budget=2048, num_requests=512, prompt=(64, 3000),
                                   output=(16, 256), seed=157010),
+    # the same, with a 1,024-token system prompt ahead of 3 in 4 prompts, served
+    # from the prefix cache after its first prefill ([L33] §6.1)
+    "replay_qwen7b_prefix": ReplayConfig("replay_qwen7b_prefix", 28, 4, 128, "bf16",
+                                         num_blocks=40000, budget=2048, num_requests=512,
+                                         prompt=(64, 3000), output=(16, 256), seed=157011,
+                                         system_prompt=1024, share=0.75),
 }
 
 
@@ -89,15 +106,17 @@ class Replay:
         self.cfg = cfg
         self.dev = device
         self.keep = keep
-        self.pool = BlockPool(cfg.num_blocks, seed=cfg.seed)
-        self.host_pool = BlockPool(cfg.host_blocks, seed=cfg.seed + 1) if cfg.host_blocks else None
+        self.pool = BlockPool(cfg.num_blocks, seed=cfg.seed, block_size=cfg.block_size)
+        self.host_pool = (BlockPool(cfg.host_blocks, seed=cfg.seed + 1, block_size=cfg.block_size)
+                          if cfg.host_blocks else None)
         self.sched = Scheduler(self.pool, cfg.budget, decode_reserve=cfg.decode_reserve,
                                host_pool=self.host_pool)
-        for r in synthetic_requests(cfg.num_requests, cfg.seed, cfg.prompt, cfg.output):
+        for r in synthetic_requests(cfg.num_requests, cfg.seed, cfg.prompt, cfg.output,
+                                    system_prompt=cfg.system_prompt, share=cfg.share):
             self.sched.add(r)
         g = torch.Generator(device=device)
         g.manual_seed(cfg.seed)
-        shape = (cfg.num_blocks, BLOCK_SIZE, cfg.num_kv_heads, cfg.head_dim)
+        shape = (cfg.num_blocks, cfg.block_size, cfg.num_kv_heads, cfg.head_dim)
         cdt = _TORCH[cfg.cache_dtype]
         # recycled blocks hold stale rows, never zeros: start from random bits
         self.k_cache = torch.randn(shape, generator=g, device=device).to(cdt)
@@ -190,8 +209,13 @@ def run(cfg: ReplayConfig, device: torch.device, max_steps: Optional[int] = None
     gpu_s = sum(r.gpu_ms for r in ss) * 1e-3
     toks = sum(r.plan.num_tokens for r in ss)
     kv = sum(r.decode_ctx_tokens for r in ss) * cfg.kv_bytes_per_token
-    return dict(steps=len(recs), steady_steps=len(ss), finished=len(rp.sched.finished),
-                preemptions=rp.sched.preemptions,
+    fin = rp.sched.finished
+    prompt_tokens = sum(r.prompt_len for r in fin)
+    saved = sum(r.hit_tokens for r in fin)
+    return dict(steps=len(recs), steady_steps=len(ss), finished=len(fin),
+                preemptions=rp.sched.preemptions, block_size=cfg.block_size,
+                prompt_tokens=prompt_tokens, prefill_tokens_saved=saved,
+                prefill_saved_frac=round(saved / max(prompt_tokens, 1), 4),
                 wall_s=round(wall, 2),
                 gpu_ms_per_step=round(gpu_s * 1e3 / len(ss), 4),
                 tokens_per_s_gpu=round(toks / gpu_s, 1),

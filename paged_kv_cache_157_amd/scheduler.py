@@ -26,6 +26,14 @@ Sources, cited by page title and section:
   [VM]  "PagedAttention: managing the KV cache like virtual memory": §3.3
         (blocks are taken as a sequence grows and returned when it ends).
 
+Prefix caching ([VM] §3.4-3.5; [L33] §6.2-6.3): a request that carries its
+prompt's token ids is admitted through the block manager's cached
+allocation, which reuses the cached blocks of its longest prefix of full
+blocks (a shared system prompt, a conversation's earlier turns), so that only
+the missed tokens are prefilled; once its prompt has been prefilled, its full
+blocks are registered as cached for later requests.  Requests without token
+ids grow their tables chunk by chunk.  The block size is the pool's.
+
 Two admission policies: with ``decode_reserve`` (the default) a prefill chunk
 is admitted only while one free block per running decode remains after it,
 so the decodes can always grow and nothing is preempted; without it chunks
@@ -44,17 +52,20 @@ from typing import Deque, List, Optional, Tuple
 
 import numpy as np
 
-from .block_manager import BLOCK_SIZE, BlockPool, PoolExhausted, SeqTable, swap_in, swap_out
+from .block_manager import BlockPool, PoolExhausted, SeqTable, swap_in, swap_out
 
 
 @dataclass
 class Request:
     """A request with a synthetic prompt length and output length (the token
-    at which it would emit end-of-sequence)."""
+    at which it would emit end-of-sequence), and optionally its prompt's token
+    ids (for prefix caching)."""
     rid: int
     prompt_len: int
     output_len: int
+    token_ids: Optional[List[int]] = None
     table: Optional[SeqTable] = None
+    hit_tokens: int = 0   # prompt tokens found in the prefix cache (no prefill)
     prefilled: int = 0    # prompt tokens whose KV is in the cache
     generated: int = 0    # output tokens produced so far
     first_step: int = -1  # step of the first chunk
@@ -166,10 +177,15 @@ class Scheduler:
         # phase 1: every running decode gets one token (its newest token's KV
         # is written and it attends everything up to it), oldest first; one
         # that finds no free block preempts the youngest until one is free
+        B = self.pool.block_size
         i = 0
         while i < len(self.running) and left > 0:
             r = self.running[i]
-            needs_block = r.table.num_tokens == len(r.table.blocks) * BLOCK_SIZE
+            # a new block is taken when the last one is full, or when the token
+            # lands in a block other tables share (copy-on-write)
+            t = r.table
+            needs_block = (t.num_tokens == len(t.blocks) * B or
+                           self.pool.ref_cnt(t.blocks[t.num_tokens // B]) > 1)
             while needs_block and self.pool.num_free == 0:
                 if self.host is None:
                     raise PoolExhausted("a decode needs a block and nothing can be preempted")
@@ -194,20 +210,35 @@ class Scheduler:
         for r in self.waiting:
             if left == 0:
                 break
+            # with the reserve: keep one free block per running decode, so that
+            # every decode can still grow by a block in the next step
+            reserve = len(self.running) if self.decode_reserve else 0
+            if r.table is None and r.token_ids is not None:
+                # admission through the prefix cache: the table covers the whole
+                # prompt at once, its cached prefix needs no prefill
+                if self.swapped:
+                    break  # preempted requests go first
+                try:
+                    r.table, r.hit_tokens = SeqTable.allocate_cached(self.pool, r.token_ids, reserve)
+                except PoolExhausted:
+                    break  # no room: this prompt and later ones wait
+                r.prefilled = r.hit_tokens
             need = r.prompt_len - r.prefilled
             n = min(need, left)
             if self.max_chunk is not None:
                 n = min(n, self.max_chunk)
-            if r.table is None:
-                r.table = SeqTable(self.pool)
-            have = len(r.table.blocks) * BLOCK_SIZE - r.table.num_tokens
-            new_blocks = -(-max(0, n - have) // BLOCK_SIZE)
-            # with the reserve: keep one free block per running decode, so that
-            # every decode can still grow by a block in the next step
-            reserve = len(self.running) if self.decode_reserve else 0
-            if (self.swapped and r.prefilled == 0) or new_blocks > self.pool.num_free - reserve:
-                break  # no room, or preempted requests go first: this prompt and later ones wait
-            slots, cows = r.table.extend(n)
+            if r.token_ids is not None:
+                # blocks already reserved for the whole prompt
+                slots = [r.table.slot(p) for p in range(r.prefilled, r.prefilled + n)]
+                cows = []
+            else:
+                if r.table is None:
+                    r.table = SeqTable(self.pool)
+                have = len(r.table.blocks) * B - r.table.num_tokens
+                new_blocks = -(-max(0, n - have) // B)
+                if (self.swapped and r.prefilled == 0) or new_blocks > self.pool.num_free - reserve:
+                    break  # no room, or preempted requests go first: this prompt and later ones wait
+                slots, cows = r.table.extend(n)
             plan.cow += cows
             if r.first_step < 0:
                 r.first_step = self.step_no
@@ -228,6 +259,10 @@ class Scheduler:
             r = c.req
             r.prefilled += c.n
             if r.prefilled == r.prompt_len:
+                if r.token_ids is not None:
+                    # the prompt's KV is in the pool: its full blocks become
+                    # reusable prefix blocks
+                    r.table.cache_full_blocks()
                 r.generated = 1
                 self.waiting.remove(r)
                 if r.generated == r.output_len:
@@ -248,10 +283,24 @@ class Scheduler:
 
 
 def synthetic_requests(n: int, seed: int, prompt: Tuple[int, int] = (64, 3000),
-                       output: Tuple[int, int] = (16, 256)) -> List[Request]:
+                       output: Tuple[int, int] = (16, 256), system_prompt: int = 0,
+                       share: float = 0.0, vocab: int = 32000) -> List[Request]:
     """``n`` requests with prompt and output lengths drawn uniformly from the
-    given closed ranges (seeded); no token ids: lengths stand in for EOS."""
+    given closed ranges (seeded); lengths stand in for EOS.  With
+    ``system_prompt`` > 0 every request carries token ids (random, seeded), and
+    a fraction ``share`` of them starts with one common system prompt of that
+    many tokens ahead of its own prompt ([L33] §6.1: a long system prompt
+    repeated across requests), which the prefix cache serves after the first
+    such request has been prefilled."""
     rng = np.random.Generator(np.random.PCG64(seed))
     p = rng.integers(prompt[0], prompt[1], size=n, endpoint=True)
     o = rng.integers(output[0], output[1], size=n, endpoint=True)
-    return [Request(i, int(a), int(b)) for i, (a, b) in enumerate(zip(p, o))]
+    if system_prompt <= 0:
+        return [Request(i, int(a), int(b)) for i, (a, b) in enumerate(zip(p, o))]
+    system = [int(x) for x in rng.integers(0, vocab, size=system_prompt)]
+    out = []
+    for i, (a, b) in enumerate(zip(p, o)):
+        own = [int(x) for x in rng.integers(0, vocab, size=int(a))]
+        ids = (system + own) if rng.random() < share else own
+        out.append(Request(i, len(ids), int(b), token_ids=ids))
+    return out

@@ -1,8 +1,10 @@
 """Continuous-batching replay on the GPU: every few steps, all outputs of the
 step (chunked prefill rows and decodes) against the oracle over the pools as
 the step left them.  Exercises block growth across block boundaries, blocks
-recycled from finished requests (holding stale rows), mixed steps and both
-decode kernels."""
+recycled from finished requests (holding stale rows), mixed steps, both
+decode kernels, preemption by swapping, prefix-cache hits (a shared system
+prompt's blocks reused by later requests, which prefill only the rest) and
+blocks of 8 and 32 tokens."""
 import numpy as np
 import pytest
 import torch
@@ -26,6 +28,17 @@ SMALL = [
     ReplayConfig("r_swap", 16, 4, 128, "bf16", num_blocks=160, budget=256, num_requests=40,
                  prompt=(16, 400), output=(20, 200), seed=6, decode_reserve=False,
                  host_blocks=400),
+    # prefix caching: a 200-token system prompt ahead of 3 in 4 prompts; later
+    # requests reuse its cached blocks and prefill only the rest
+    ReplayConfig("r_prefix", 8, 2, 128, "bf16", num_blocks=300, budget=256, num_requests=24,
+                 prompt=(1, 300), output=(1, 40), seed=73, system_prompt=200, share=0.75),
+    # 8-token blocks (the one-KV-head decode kernel)
+    ReplayConfig("r_b8", 16, 4, 128, "bf16", num_blocks=460, budget=256, num_requests=24,
+                 prompt=(1, 300), output=(1, 40), seed=74, block_size=8),
+    # 32-token blocks, head groups, fp8, with prefix hits
+    ReplayConfig("r_b32_prefix", 32, 8, 128, "fp8", num_blocks=150, budget=256, num_requests=24,
+                 prompt=(1, 300), output=(1, 40), seed=75, kv_scale=0.05, block_size=32,
+                 system_prompt=100, share=0.75),
 ]
 
 
@@ -47,11 +60,12 @@ def test_replay_steps_match_the_oracle(cfg):
         if st["pre"] is not None:
             bt, qs, ctx = st["pre"]["host"]
             ref = oracle.prefill(q[:st["n_pre"]], kp, vp, bt, qs, ctx, cfg.scale,
-                                 kv_scale=cfg.kv_scale)
+                                 kv_scale=cfg.kv_scale, block_size=cfg.block_size)
             assert max_err(out[:st["n_pre"]], ref) <= TOL[cfg.cache_dtype]
         if st["dec"] is not None:
             bt, lens = st["dec"]["host"]
-            ref = oracle.decode(q[st["n_pre"]:], kp, vp, bt, lens, cfg.scale, kv_scale=cfg.kv_scale)
+            ref = oracle.decode(q[st["n_pre"]:], kp, vp, bt, lens, cfg.scale, kv_scale=cfg.kv_scale,
+                                block_size=cfg.block_size)
             assert max_err(out[st["n_pre"]:], ref) <= TOL[cfg.cache_dtype]
         checked += 1
         mixed += st["pre"] is not None and st["dec"] is not None
@@ -59,4 +73,9 @@ def test_replay_steps_match_the_oracle(cfg):
     assert checked >= 10 and mixed >= 3
     if not cfg.decode_reserve:
         assert rp.sched.preemptions > 0
+    if cfg.system_prompt:
+        hits = [r.hit_tokens for r in rp.sched.finished]
+        say(f"replay {cfg.name}: {sum(h > 0 for h in hits)} of {len(hits)} requests hit the "
+            f"prefix cache, {sum(hits)} prompt tokens not prefilled")
+        assert sum(h > 0 for h in hits) >= cfg.num_requests // 2
     assert rp.pool.num_free == cfg.num_blocks  # every block returned
