@@ -7,16 +7,21 @@
 //
 // Here the query tile makes QK^T a dense contraction, so it runs on the
 // matrix cores (v_mfma_f32_32x32x16_bf16):
-//   * A work-group (8 waves, two per SIMD so that one wave's softmax overlaps
-//     the other's matrix products) owns 256 "query rows" = (position, head)
-//     pairs of one KV head (all G heads of a position are adjacent, so one K/V
-//     tile feeds every head of the group), and one slice of the key range.
-//     Each wave holds one 32-row MFMA block.
+//   * A work-group (8 waves, two per SIMD) owns 256 "query rows" = (position,
+//     head) pairs of one KV head (all G heads of a position are adjacent, so
+//     one K/V tile feeds every head of the group), and one slice of the key
+//     range.  Each wave holds one 32-row MFMA block.
+//   * With a bf16 cache the two waves of a SIMD take turns (waves 0-3 and
+//     4-7, half a tile apart, a work-group barrier between turns): one runs
+//     its matrix phase (P V of the previous tile, S^T of this one) while the
+//     other runs its vector phase (mask, maximum, exponentials, row sum, P in
+//     bf16), so the matrix core and the vector ALU of a SIMD work at the same
+//     time.  With an fp8 cache every wave runs a tile's steps in order.
 //   * Per 64-key tile, K and V rows are gathered through the block table
 //     straight into LDS (global_load_lds, 16 bytes per lane) through a ring of
-//     four tiles, so three tiles are in flight while one is computed; each wave
-//     counts its own loads (s_waitcnt vmcnt) and one work-group barrier per
-//     tile publishes them.  Both tiles stay row-major with XOR-swizzled
+//     four tiles, so two or three tiles are in flight while one is computed;
+//     each wave counts its own loads (s_waitcnt vmcnt) and a work-group
+//     barrier publishes a tile.  Both tiles stay row-major with XOR-swizzled
 //     16-byte chunks: K fragments (MFMA A operand, 16 bytes per lane) and V^T
 //     fragments (B operand, via the gfx950 transposing LDS read) come out
 //     without bank conflicts.  fp8 rows arrive raw and are widened to bf16
@@ -67,6 +72,7 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi)
 
 constexpr int kPrefillWaves = 8;  // two per SIMD
 constexpr int kPrefillThreads = 64 * kPrefillWaves;
+
 
 template <int CDT, int D>
 struct PrefillCfg {
@@ -165,6 +171,13 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p)
 {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char *)p;
 }
+// keep(x): an empty asm that takes x in registers and may change it, so the
+// computation of x cannot move past this point (the optimiser would otherwise
+// sink pure arithmetic to where its result is used)
+__device__ __forceinline__ void keep(float &x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void keep(u32x4 &x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void keep(f32x16 &x) { asm volatile("" : "+v"(x)); }
+
 // Work-group barrier that drains this wave's LDS operations only: the
 // global->LDS loads of later tiles stay in flight (__syncthreads would wait
 // for them too).
@@ -414,7 +427,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
     // ---- S^T = K Q^T of one tile (both 32-key halves) -------------------------------
     // K fragments are read two 16-d steps ahead of their products, so the LDS
     // latency of a step overlaps the products of the two before it
-    auto s_tile = [&](const char *kt_lds, f32x16 (&s)[2]) {
+    auto s_tile = [&](const char *kt_lds, f32x16 (&s)[2], auto pin_) {
         constexpr int AH = ST < 3 ? ST : 3;  // steps of fragments in flight
         u32x4 ka[AH][2];
         auto read = [&](int st) {
@@ -438,13 +451,15 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
         // keep that order through scheduling (which would otherwise sink each
         // read to its product to save registers): the first reads, then per
         // step two products and the reads of a later step
-        __builtin_amdgcn_sched_group_barrier(0x100, 2 * (AH - 1), 0);
-        static_for<ST>([&](auto st_) {
-            constexpr int st = decltype(st_)::value;
-            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-            if constexpr (st + AH - 1 < ST)
-                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-        });
+        if constexpr (decltype(pin_)::value) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 2 * (AH - 1), 0);
+            static_for<ST>([&](auto st_) {
+                constexpr int st = decltype(st_)::value;
+                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+                if constexpr (st + AH - 1 < ST)
+                    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            });
+        }
     };
     // ---- mask (diagonal / ragged tiles only), row maximum, lazy rescale --------------
     // Raises the running maximum when the tile exceeds it by more than TAU
@@ -491,16 +506,13 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
         // a row with no valid key yet keeps mref = -inf: its probabilities are 0
         return mref == -INFINITY ? 0.f : mref;
     };
-    // ---- probabilities and O += P V, four 16-key steps --------------------------------
-    // MODE 0 (bf16 caches): P as a bf16 head and a bf16 tail (weights exact to
-    // ~2^-16); 1 (fp8 caches): one bf16 rounding of P, and the rounded weights
-    // enter the row sum as they enter the products, so the result stays a
-    // convex combination of V rows (a row with one key returns its value
-    // exactly); that sum is formed with v_dot2 against (1, 1): exact products,
-    // one fp32 sum per pair (four VALU instructions fewer per pair than
-    // widening both halves and adding them).
-    auto pv_tile = [&](const f32x16 (&s)[2], float mu, const char *vt_lds, auto mode_) {
-        constexpr int MODE = decltype(mode_)::value;
+    // ---- fp8 caches: probabilities and O += P V, four 16-key steps ----------------
+    // One bf16 rounding of P, and the rounded weights enter the row sum as they
+    // enter the products, so the result stays a convex combination of V rows
+    // (a row with one key returns its value exactly); that sum is formed with
+    // v_dot2 against (1, 1): exact products, one fp32 sum per pair (four VALU
+    // instructions fewer per pair than widening both halves and adding them).
+    auto pv_tile = [&](const f32x16 (&s)[2], float mu, const char *vt_lds) {
         static_for<4>([&](auto ks_) {
             constexpr int ks = decltype(ks_)::value;
             constexpr int kc = ks >> 1, h8 = ks & 1;
@@ -520,75 +532,193 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
             for (int j = 0; j < 8; ++j)
                 p[j] = fast_exp2(fmaf(s[kc][8 * h8 + j], c, -mu));
             uint32_t h[4];
-            if constexpr (MODE == 1) {
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    h[j] = pack_bf16(p[2 * j], p[2 * j + 1]);
-                    lsum = dot2_bf16(h[j], kBf16OnePair, lsum);
-                }
-                const u32x4 ph = u32x4{h[0], h[1], h[2], h[3]};
+            for (int j = 0; j < 4; ++j) {
+                h[j] = pack_bf16(p[2 * j], p[2 * j + 1]);
+                lsum = dot2_bf16(h[j], kBf16OnePair, lsum);
+            }
+            const u32x4 ph = u32x4{h[0], h[1], h[2], h[3]};
 #pragma unroll
-                for (int dt = 0; dt < D / 32; ++dt) {
-                    const u32x4 vb =
-                        u32x4{vr[2 * dt][0], vr[2 * dt][1], vr[2 * dt + 1][0], vr[2 * dt + 1][1]};
-                    o[dt] = mfma32(ph, vb, o[dt]);
-                }
-            } else {
-#pragma unroll
-                for (int j = 0; j < 8; ++j)
-                    lsum += p[j];
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    h[j] = pack_bf16(p[2 * j], p[2 * j + 1]);
-                const u32x4 ph = u32x4{h[0], h[1], h[2], h[3]};
-                uint32_t t[4];
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    t[j] = pack_bf16(p[2 * j] - bf16_lo(h[j]), p[2 * j + 1] - bf16_hi(h[j]));
-                const u32x4 pl = u32x4{t[0], t[1], t[2], t[3]};
-#pragma unroll
-                for (int dt = 0; dt < D / 32; ++dt) {
-                    const u32x4 vb =
-                        u32x4{vr[2 * dt][0], vr[2 * dt][1], vr[2 * dt + 1][0], vr[2 * dt + 1][1]};
-                    o[dt] = mfma32(ph, vb, o[dt]);
-                    o[dt] = mfma32(pl, vb, o[dt]);
-                }
+            for (int dt = 0; dt < D / 32; ++dt) {
+                const u32x4 vb = u32x4{vr[2 * dt][0], vr[2 * dt][1], vr[2 * dt + 1][0], vr[2 * dt + 1][1]};
+                o[dt] = mfma32(ph, vb, o[dt]);
             }
         });
     };
 
-    auto compute_tile = [&](const char *kt_lds, const char *vt_lds, int kt, auto mode) {
+    using Pinned = std::true_type;
+    auto compute_tile = [&](const char *kt_lds, const char *vt_lds, int kt) {
         f32x16 s[2];
-        s_tile(kt_lds, s);
+        s_tile(kt_lds, s, Pinned{});
         const float mu = mask_max(s, kt);
-        pv_tile(s, mu, vt_lds, mode);
+        pv_tile(s, mu, vt_lds);
     };
-    using Mode0 = std::integral_constant<int, 0>;
-    using Mode1 = std::integral_constant<int, 1>;
-    // The table entries of the next tile to issue are read one iteration ahead,
-    // at the end of the compute: the barrier's wait then covers their latency
-    // instead of every wave stalling on them right after it.
+
+    // ---- bf16 caches: the tile work as a vector and a matrix phase --------------
+    // vec: mask, maximum, exponentials, row sum, and P as a bf16 head and a bf16
+    // tail (weights exact to ~2^-16; a single bf16 rounding costs up to 2^-8
+    // relative weight error, too coarse for rows with few keys at that cache's
+    // precision); mat: P V of the previous tile (head and tail), then S^T of
+    // this one.
+    auto probs0 = [&](const f32x16 (&s)[2], float mu, u32x4 (&ph)[4], u32x4 (&pl)[4]) {
+        static_for<4>([&](auto ks_) {
+            constexpr int ks = decltype(ks_)::value;
+            constexpr int kc = ks >> 1, h8 = ks & 1;
+            float p[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                p[j] = fast_exp2(fmaf(s[kc][8 * h8 + j], c, -mu));
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                lsum += p[j];
+            uint32_t h[4], t[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                h[j] = pack_bf16(p[2 * j], p[2 * j + 1]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                t[j] = pack_bf16(p[2 * j] - bf16_lo(h[j]), p[2 * j + 1] - bf16_hi(h[j]));
+            ph[ks] = u32x4{h[0], h[1], h[2], h[3]};
+            pl[ks] = u32x4{t[0], t[1], t[2], t[3]};
+        });
+    };
+    auto pv0 = [&](const u32x4 (&ph)[4], const u32x4 (&pl)[4], const char *vt_lds) {
+        // V^T fragments of step ks + 1 are read while the products of step ks run
+        lds_char *vt3 = (lds_char *)vt_lds;
+        u32x4 vb[2][D / 32];
+        auto read = [&](int ks) {
+#pragma unroll
+            for (int dt = 0; dt < D / 32; ++dt) {
+                lds_char *vp = vt3 + vofs[dt] + 16 * ks * ROWB;
+                const u32x2 a0 = lds_read_tr16(vp), a1 = lds_read_tr16(vp + 8 * ROWB);
+                vb[ks & 1][dt] = u32x4{a0[0], a0[1], a1[0], a1[1]};
+            }
+        };
+        read(0);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            if (ks + 1 < 4)
+                read(ks + 1);
+#pragma unroll
+            for (int dt = 0; dt < D / 32; ++dt)
+                o[dt] = mfma32(ph[ks], vb[ks & 1][dt], o[dt]);
+#pragma unroll
+            for (int dt = 0; dt < D / 32; ++dt)
+                o[dt] = mfma32(pl[ks], vb[ks & 1][dt], o[dt]);
+        }
+        // pin that order: reads of step 0, then per step its products and the
+        // reads of the next
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * (D / 32), 0);
+        static_for<4>([&](auto ks_) {
+            constexpr int ks = decltype(ks_)::value;
+            if constexpr (ks + 1 < 4)
+                __builtin_amdgcn_sched_group_barrier(0x100, 2 * (D / 32), 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 2 * (D / 32), 0);
+        });
+    };
+    // work-group barrier between phases; nothing is scheduled across it
+    // (and keep() below stops the optimiser from sinking a phase's arithmetic
+    // into the next one, where its results are used)
+    auto phase_barrier = [&]() {
+        __builtin_amdgcn_sched_barrier(0);
+        barrier_lds();
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    constexpr bool PP = !C::RAW;  // bf16 caches: the two waves of a SIMD take turns
+    // The table entries of the next tile to issue are read right after a tile
+    // is issued (fp8: at the end of the compute), so their scalar loads are in
+    // flight while other work runs.
     Units pbn = {};
-    if constexpr (!C::RAW) {
-        // the ring stages are the compute tiles
-        for (int u = 0; u < NS - 1 && u < nt; ++u) {
+    if constexpr (PP) {
+        // Waves 0-3 and 4-7 (one of each per SIMD) run the phases half a tile
+        // apart: in phase 2u the first group does mat(u) while the second does
+        // vec(u - 1); in phase 2u + 1 the first does vec(u), the second mat(u).
+        // A barrier separates phases, so while one wave of a SIMD keeps the
+        // matrix core busy the other has the vector ALU.  Tile t is read in
+        // phases 2t .. 2t + 3, so with four ring stages tile u + 2 is issued
+        // at the start of phase 2u into the stage tile u - 2 has left.
+        // waves w and w + 4 share a SIMD (work-group waves are placed on the
+        // four SIMDs in turn); the matrix phase runs at raised issue priority
+        const bool mat_first = w < C::WAVES / 2;
+        f32x16 s[2];
+        u32x4 ph[4], pl[4];
+        // Every wave runs the same sequence S(0), vec(0), PV(0) + S(1), vec(1),
+        // ..., PV(nt - 1) with a barrier before each phase; the second group
+        // passes one extra barrier first and the first group one at the end,
+        // which puts them a phase apart.  The ring work of phase p (tile p / 2
+        // landed and published, tile p / 2 + 2 issued) happens at the barrier
+        // before phase p, whichever of its phases a wave is in.
+        int gp = 0;  // global index of the phase about to start
+        auto boundary = [&]() {
+            if ((gp & 1) == 0) {
+                const int u = gp >> 1;
+                if (u < nt)
+                    wait_tiles_in_flight<DPW>(nt - 1 - u < 1 ? nt - 1 - u : 1);  // tile u landed
+                phase_barrier();  // tile u visible to all; tile u - 2's stage is free
+                if (u + 2 < nt)
+                    issue_tile(t0 + u + 2, (u + 2) % NS, pbn);
+                if (u + 3 < nt)
+                    tile_units(t0 + u + 3, pbn);
+            } else {
+                phase_barrier();
+            }
+            ++gp;
+        };
+        auto stage = [&](int u) { return sm.ring + (u % NS) * C::STAGEB; };
+        auto vec = [&](int u) {
+            const float mu = mask_max(s, t0 + u);
+            probs0(s, mu, ph, pl);
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                keep(ph[ks]);
+                keep(pl[ks]);
+            }
+            keep(lsum);
+        };
+        auto kept_s = [&]() {
+            keep(s[0]);
+            keep(s[1]);
+        };
+        auto kept_o = [&]() {
+#pragma unroll
+            for (int dt = 0; dt < D / 32; ++dt)
+                keep(o[dt]);
+        };
+        for (int u = 0; u < 2 && u < nt; ++u) {
             tile_units(t0 + u, pbn);
             issue_tile(t0 + u, u, pbn);
         }
-        if (NS - 1 < nt)
-            tile_units(t0 + NS - 1, pbn);
-        for (int u = 0; u < nt; ++u) {
-            const int kt = t0 + u;
-            const int ahead = nt - 1 - u < NS - 2 ? nt - 1 - u : NS - 2;
-            wait_tiles_in_flight<DPW>(ahead);  // tile u landed
-            barrier_lds();  // tile u visible to all; stage (u - 1) % NS is free
-            if (u + NS - 1 < nt)
-                issue_tile(kt + NS - 1, (u + NS - 1) % NS, pbn);
-            const char *st_lds = sm.ring + (u % NS) * C::STAGEB;
-            compute_tile(st_lds, st_lds + C::TILEB, kt, Mode0{});
-            if (u + NS < nt)
-                tile_units(kt + NS, pbn);
+        if (2 < nt)
+            tile_units(t0 + 2, pbn);
+        if (!mat_first)
+            boundary();
+        boundary();
+        if (nt > 0) {
+            __builtin_amdgcn_s_setprio(1);
+            s_tile(stage(0), s, Pinned{});
+            __builtin_amdgcn_s_setprio(0);
+            kept_s();
+            for (int u = 0; u + 1 < nt; ++u) {
+                boundary();
+                vec(u);
+                boundary();
+                __builtin_amdgcn_s_setprio(1);
+                pv0(ph, pl, stage(u) + C::TILEB);
+                s_tile(stage(u + 1), s, Pinned{});
+                __builtin_amdgcn_s_setprio(0);
+                kept_s();
+                kept_o();
+            }
+            boundary();
+            vec(nt - 1);
+            boundary();
+            __builtin_amdgcn_s_setprio(1);
+            pv0(ph, pl, stage(nt - 1) + C::TILEB);
+            __builtin_amdgcn_s_setprio(0);
+            kept_o();
         }
+        if (mat_first)
+            boundary();
     } else {
         // raw ring -> widened double buffer, one tile ahead of the compute
         for (int u = 0; u < NS - 1 && u < nt; ++u) {
@@ -612,7 +742,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
             if (u + NS - 1 < nt)
                 issue_tile(kt + NS - 1, (u + NS - 1) % NS, pbn);
             const char *cb_lds = sm.ring + NS * C::STAGEB + (u & 1) * 2 * C::TILEB;
-            compute_tile(cb_lds, cb_lds + C::TILEB, kt, Mode1{});
+            compute_tile(cb_lds, cb_lds + C::TILEB, kt);
             if (u + 1 < nt)
                 widen_tile((u + 1) % NS, (u + 1) & 1);
             if (u + NS < nt)

@@ -193,6 +193,12 @@ def test_prefill_split_merge(storage, hist, chunk, hq, hkv):
     say(f"  max |err| = {err:.3e}")
     assert np.all(np.isfinite(out.cpu().numpy()))
     assert err <= TOL[storage]
+    # the merge order is fixed: a second call gives the same bits
+    again = torch.full(qp.shape, float("nan"), dtype=torch.float32, device="cuda")
+    binding.prefill_chunk(again, qp, p["k"], p["v"], p["bt"], to_dev(qs), p["lens"], p["scale"],
+                          kv_scale=p["kv_scale"])
+    torch.cuda.synchronize()
+    assert torch.equal(out, again)
 
 
 def test_decode_on_two_streams_at_once():
