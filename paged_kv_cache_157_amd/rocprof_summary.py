@@ -2,6 +2,7 @@
 
     python -m paged_kv_cache_157_amd.rocprof_summary stats <out_dir> <out.md> <command...>
     python -m paged_kv_cache_157_amd.rocprof_summary traffic <rd_dir> <wr_dir> <workload> <out.md> <command...>
+    python -m paged_kv_cache_157_amd.rocprof_summary line <out.md> <title> <json_file>... -- <command...>
 
 `stats` reads the kernel statistics and the kernel trace of one
 `rocprofv3 --kernel-trace --stats` run.  Besides the per-kernel table it
@@ -21,6 +22,10 @@ both against its known size, and the FETCH_SIZE formula's value is shown
 beside them.  Bytes per decode launch go to profiles/traffic.json together
 with a hash of the decode source, so bench.py reports the figure only while
 the kernel is unchanged.
+
+`line` keeps bench.py result lines (the last JSON line of each file) as a
+short markdown summary with the command that printed them: the scalar fields
+of each line, and those of its nested records, one table per line.
 """
 from __future__ import annotations
 
@@ -193,11 +198,38 @@ def traffic(rd_dir: str, wr_dir: str, workload: str, out_md: str, command: str) 
     print("\n".join(lines))
 
 
+def _flat(rec: dict, prefix: str = "") -> list:
+    rows = []
+    for k, v in rec.items():
+        if isinstance(v, dict):
+            rows += _flat(v, f"{prefix}{k}.")
+        elif isinstance(v, list):
+            rows.append((prefix + k, json.dumps(v)))
+        else:
+            rows.append((prefix + k, v))
+    return rows
+
+
+def line(out_md: str, title: str, files: list, command: str) -> None:
+    out = [f"# {title}", "", f"Command: `{command}`", ""]
+    for f in files:
+        rec = json.loads(open(f).read().strip().splitlines()[-1])
+        out += [f"## {rec.get('config', {}).get('workload', rec.get('metric', f))}", "",
+                "| field | value |", "|---|---|"]
+        out += [f"| {k} | {v} |" for k, v in _flat(rec)]
+        out.append("")
+    open(out_md, "w").write("\n".join(out))
+    print(f"wrote {out_md}")
+
+
 if __name__ == "__main__":
     mode = sys.argv[1]
     if mode == "stats":
         stats(sys.argv[2], sys.argv[3], " ".join(sys.argv[4:]))
     elif mode == "traffic":
         traffic(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5], " ".join(sys.argv[6:]))
+    elif mode == "line":
+        sep = sys.argv.index("--")
+        line(sys.argv[2], sys.argv[3], sys.argv[4:sep], " ".join(sys.argv[sep + 1:]))
     else:
         raise SystemExit(__doc__)
