@@ -24,12 +24,13 @@ The roofline entry is for the decode launch (one kernel):
     launch (a 768 MiB read in between, subtracted), median and minimum, which
     is what a model's layer sees when it reads its KV once per step.
 The cache write, shorter than one host submission, is timed over launches
-queued behind a GPU-side wait.  Unless --no-configs is given, the other
+queued behind a GPU-side wait.  As context for the 8 TB/s peak the line
+also gives the box's read-stream bandwidth (the cold leg's 768 MiB reads
+alone) and a plain 1 GiB device copy.  Unless --no-configs is given, the other
 workloads (13B MHA with a shared prefix, the skewed long/short mix, and the
 chunked-prefill mixed step with bf16 and fp8 caches) follow, each with the
 same W warm-up and K timed steps, and go into `configs`.
-``--extras`` adds a plain device copy, the block copy and swap kernels and
-the block-size sweep.  A replay_* workload runs the continuous-batching
+``--extras`` adds the block copy and swap kernels and the block-size sweep.  A replay_* workload runs the continuous-batching
 replay instead and reports its steady state.
 """
 from __future__ import annotations
@@ -67,8 +68,8 @@ def parse():
     ap.add_argument("--no-cold", action="store_true",
                     help="skip the decode with the Infinity Cache evicted")
     ap.add_argument("--extras", action="store_true",
-                    help="also measure a plain device copy, pa_copy_blocks, pa_swap_blocks and "
-                         "the block-size sweep (after the timed steps)")
+                    help="also measure pa_copy_blocks, pa_swap_blocks and the block-size sweep "
+                         "(after the timed steps)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB "
                          "(a known-size reference for hardware byte counters)")
@@ -229,8 +230,9 @@ class Timer:
         """Launch time of fn with its inputs evicted from the 256 MB Infinity
         Cache: n rounds of (a read of `evict`, larger than that cache, then fn)
         back to back, minus n reads alone, per round; median and minimum over
-        `reps` repetitions."""
-        ts = []
+        `reps` repetitions.  The reads alone also give the box's read-stream
+        bandwidth (median over the repetitions)."""
+        ts, rd = [], []
         for _ in range(reps):
             t = []
             for with_fn in (True, False):
@@ -245,8 +247,9 @@ class Timer:
                 torch.cuda.synchronize()
                 t.append(self.e0.elapsed_time(self.e1))
             ts.append((t[0] - t[1]) / n * 1e3)
+            rd.append(n * evict.numel() * evict.element_size() / (t[1] * 1e-3) / 1e9)
         return dict(median_us=round(float(np.median(ts)), 2), min_us=round(float(np.min(ts)), 2),
-                    launches=n * reps)
+                    launches=n * reps, read_stream_gbs=round(float(np.median(rd)), 1))
 
 
 def prefill_flops(cfg) -> int:
@@ -460,19 +463,17 @@ def main():
                                   tail_waste_tokens=int((nbs * B - L).sum()))
             del kb, vb
 
-    copy_gbs = None
-    if args.extras:
-        # bandwidth context: a plain 1 GiB device copy (reads and writes 1 GiB)
-        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
+    # bandwidth context: a plain 1 GiB device copy (reads and writes 1 GiB)
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    timer.e0.record()
+    for _ in range(5):
         dst.copy_(src)
-        timer.e0.record()
-        for _ in range(5):
-            dst.copy_(src)
-        timer.e1.record()
-        torch.cuda.synchronize()
-        copy_gbs = round(2 * (1 << 30) * 5 / (timer.e0.elapsed_time(timer.e1) * 1e-3) / 1e9, 1)
-        del src, dst
+    timer.e1.record()
+    torch.cuda.synchronize()
+    copy_gbs = round(2 * (1 << 30) * 5 / (timer.e0.elapsed_time(timer.e1) * 1e-3) / 1e9, 1)
+    del src, dst
     if args.copy_probe_mib:
         # a plain device copy of known size: rocprofv3 --pmc reads of FETCH_SIZE /
         # WRITE_SIZE for it convert the counters into bytes
@@ -512,6 +513,7 @@ def main():
 
     dec_us = head["decode_us"]
     cold = head.get("decode_cold")
+    read_gbs = cold.pop("read_stream_gbs", None) if cold else None
     res = {
         "metric": METRIC,
         "value": head["step_kv_gbs"],
@@ -547,6 +549,7 @@ def main():
                          cold, timing="Infinity Cache evicted before every launch (768 MiB read, "
                                       "subtracted); median and minimum over 5 x 20 launches")},
         "device_copy_gbs": copy_gbs,
+        "read_stream_gbs": read_gbs,
         "copy_blocks": copy_res,
         "swap_blocks": swap_res,
         "block_size_sweep": bs_res,
