@@ -630,15 +630,15 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
     // flight while other work runs.
     Units pbn = {};
     if constexpr (PP) {
-        // Waves 0-3 and 4-7 (one of each per SIMD) run the phases half a tile
+        // Waves w and w + 4 share a SIMD (work-group waves are placed on the
+        // four SIMDs in turn).  Waves 0-3 and 4-7 run the phases half a tile
         // apart: in phase 2u the first group does mat(u) while the second does
         // vec(u - 1); in phase 2u + 1 the first does vec(u), the second mat(u).
         // A barrier separates phases, so while one wave of a SIMD keeps the
-        // matrix core busy the other has the vector ALU.  Tile t is read in
-        // phases 2t .. 2t + 3, so with four ring stages tile u + 2 is issued
-        // at the start of phase 2u into the stage tile u - 2 has left.
-        // waves w and w + 4 share a SIMD (work-group waves are placed on the
-        // four SIMDs in turn); the matrix phase runs at raised issue priority
+        // matrix core busy (at raised issue priority) the other has the vector
+        // ALU.  Tile t is read in phases 2t .. 2t + 3, so with four ring stages
+        // tile u + 2 is issued at the start of phase 2u into the stage tile
+        // u - 2 has left.
         const bool mat_first = w < C::WAVES / 2;
         f32x16 s[2];
         u32x4 ph[4], pl[4];
