@@ -527,20 +527,20 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(DecodeArgs a)
                 wait_vm<0>();
         }
 
-        // ---- wave totals -> LDS --------------------------------------------
+        // ---- wave totals -> LDS, in the folded order of fold_totals: element
+        // (h, e) of piece p at h * D + e * NCV + p --------------------------------
         const float ls = dec::token_total<LPT>(lane_owner ? lsum : 0.f);
+        {
+            constexpr int Q = G * EV / 4;
+            float tot[Q];
+            dec::fold_totals<G, EV, VTPR>(acc, tot);
+            const int p = lane & 15, r = lane >> 4;
+            if (p < NCV) {
+                float *accw = (float *)&sm.ring[w][NSTAGE - 1][0] + r * Q * NCV + p;
 #pragma unroll
-        for (int h = 0; h < G; ++h)
-#pragma unroll
-            for (int e = 0; e < EV; ++e)
-                acc[h][e] = dec::piece_total<VTPR>(acc[h][e]);
-        if (lane < NCV) {
-            float *accw = (float *)&sm.ring[w][NSTAGE - 1][0];
-#pragma unroll
-            for (int h = 0; h < G; ++h)
-#pragma unroll
-                for (int e = 0; e < EV; ++e)
-                    accw[h * D + lane * EV + e] = acc[h][e];
+                for (int k = 0; k < Q; ++k)
+                    accw[k * NCV] = tot[k];
+            }
         }
         if (lane < 16 && tr == 0 && lane_owner)
             sm.msum[w][1][lane_m] = ls;
@@ -551,10 +551,17 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(DecodeArgs a)
         }
         barrier_lds();
 
-        // ---- merge the waves; write the output, or a partial -----------------
-        // two consecutive d of one head per thread
-        for (int e = 2 * tid; e < G * D; e += 2 * NT) {
-            const int h = e / D, c = e - h * D;
+        // ---- merge the waves; write the output, or a partial (kept in the
+        // folded order) -----------------------------------------------------------
+        // two neighbouring folded positions (pieces p, p + 1 of one element e)
+        // per thread; a fixed trip count lets every LDS read go out at once
+        constexpr int MPAIRS = G * D / 2, MITER = (MPAIRS + NT - 1) / NT;
+#pragma unroll
+        for (int it = 0; it < MITER; ++it) {
+            const int f = 2 * (tid + it * NT);
+            if (MPAIRS % NT != 0 && f >= G * D)
+                break;
+            const int h = f / D, q = f - h * D;
             float M = -INFINITY;
 #pragma unroll
             for (int ww = 0; ww < WAVES; ++ww)
@@ -563,22 +570,23 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(DecodeArgs a)
 #pragma unroll
             for (int ww = 0; ww < WAVES; ++ww) {
                 const float m = sm.msum[ww][0][h];
-                const float f = m == -INFINITY ? 0.f : fast_exp2(m - M);
+                const float fw = m == -INFINITY ? 0.f : fast_exp2(m - M);
                 const float *accw = (const float *)&sm.ring[ww][NSTAGE - 1][0];
-                A0 += f * accw[h * D + c];
-                A1 += f * accw[h * D + c + 1];
-                Ls += f * sm.msum[ww][1][h];
+                A0 += fw * accw[f];
+                A1 += fw * accw[f + 1];
+                Ls += fw * sm.msum[ww][1][h];
             }
             if (direct) {
-                float *dst = a.out + ((int64_t)i * Hq + g * G + h) * D + c;
+                const int e = q / NCV, p = q - e * NCV;  // columns p * EV + e and (p + 1) * EV + e
+                float *dst = a.out + ((int64_t)i * Hq + g * G + h) * D + p * EV + e;
                 const float inv = a.v_scale / Ls;
                 dst[0] = A0 * inv;
-                dst[1] = A1 * inv;
+                dst[EV] = A1 * inv;
             } else {
                 // partials are written and read with device-coherent (L2-bypassing)
                 // accesses, so the hand-over below needs no cache flush
-                coherent_store2(&a.ws_acc[((int64_t)slot * G + h) * D + c], A0, A1);
-                if (c == 0)
+                coherent_store2(&a.ws_acc[((int64_t)slot * G + h) * D + q], A0, A1);
+                if (q == 0)
                     coherent_store2(&a.ws_ml[((int64_t)slot * G + h) * 2], M, Ls);
             }
         }
@@ -605,7 +613,7 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(DecodeArgs a)
                                                  __HIP_MEMORY_SCOPE_AGENT) == hi - lo;
             barrier_lds();
             if (sm.last) {
-                dec::merge_partials<G, D, NT, 8>(a.ws_ml, a.ws_acc, lo, hi - lo + 1,
+                dec::merge_partials<G, D, NT, 8, NCV>(a.ws_ml, a.ws_acc, lo, hi - lo + 1,
                                                  a.out + ((int64_t)i * Hq + g * G) * D, a.v_scale, tid,
                                                  sm.merge);
                 if (tid == 0)

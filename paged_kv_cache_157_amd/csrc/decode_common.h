@@ -190,6 +190,46 @@ __device__ __forceinline__ float piece_total(float v)
     return v;
 }
 
+// The wave totals of all G x EV accumulator elements of a lane at once,
+// summed over rows by a reduce-scatter.  Swapping two *different* values
+// across the wave halves gives every lane one half-partial of each, so one
+// swap and one add fold the halves of two elements where sum_rows folds one;
+// a second level does the same across neighbouring rows.  Afterwards register
+// k of a lane in row r holds element j = r * (G * EV / 4) + k (j = h * EV + e)
+// summed over the four rows, in the same order of additions as sum_rows; the
+// lanes of a row that accumulate other tokens of the same V piece are then
+// added as in piece_total.  A quarter of the lane swaps and adds of
+// piece_total on every element.
+template <int G, int EV, int VTPR>
+__device__ __forceinline__ void fold_totals(const float (&acc)[G][EV], float (&out)[G * EV / 4])
+{
+    constexpr int V = G * EV, H = V / 2, Q = V / 4;
+    static_assert(V % 4 == 0, "fold needs a multiple of 4 elements");
+    float t[H];
+#pragma unroll
+    for (int k = 0; k < H; ++k) {
+        // rows 0-1 end with element k, rows 2-3 with element k + H
+        const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[k / EV][k % EV]),
+                                                        __float_as_uint(acc[(k + H) / EV][(k + H) % EV]),
+                                                        false, false);
+        t[k] = __uint_as_float(s[0]) + __uint_as_float(s[1]);
+    }
+#pragma unroll
+    for (int k = 0; k < Q; ++k) {
+        // row 0: element k, row 1: k + Q, row 2: k + 2Q, row 3: k + 3Q
+        const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(t[k]), __float_as_uint(t[k + Q]), false,
+                                                        false);
+        float x = __uint_as_float(s[0]) + __uint_as_float(s[1]);
+        if constexpr (VTPR == 2)
+            x += dpp<DPP_ROW_ROR8>(x);
+        if constexpr (VTPR == 4) {
+            x += dpp<DPP_ROW_ROR4>(x);
+            x += dpp<DPP_ROW_ROR8>(x);
+        }
+        out[k] = x;
+    }
+}
+
 // Inclusive prefix sum over the 64 lanes of a wave (32-bit): shifts within
 // rows of 16, then the row totals carried over with row broadcasts.
 __device__ __forceinline__ int wave_scan32(int x)
@@ -509,7 +549,9 @@ struct MergeLds {
 // Log-sum-exp merge of the np partial records [lo, lo + np) of one pair into
 // its output row (HEADS query heads x D): record s holds, for each head h, the
 // running maximum and sum (ml[(s * HEADS + h) * 2 + 0/1], base 2) and the
-// unnormalised accumulator (acc[(s * HEADS + h) * D + c]).  Records are read
+// unnormalised accumulator (acc[(s * HEADS + h) * D + c]; with FOLD_NCV > 0
+// the D values of a head are in the folded order of fold_totals: position
+// (d % EV) * FOLD_NCV + d / EV holds column d, EV = D / FOLD_NCV).  Records are read
 // in batches of MB: every thread issues the accumulator loads of its columns
 // (4 consecutive d each), the threads that own a head load the (max, sum)
 // pairs and publish the batch's scale factors through LDS, then all combine:
@@ -517,7 +559,7 @@ struct MergeLds {
 // fewer where prefetched blocks occupy them.  Records are read with
 // device-coherent loads (their writers stored them the same way).  Called by
 // every thread of the work-group (it holds work-group barriers).
-template <int HEADS, int D, int NT, int MB, int MBMAX>
+template <int HEADS, int D, int NT, int MB, int FOLD_NCV, int MBMAX>
 __device__ __forceinline__ void merge_partials(const float *ws_ml, const float *ws_acc, int lo, int np,
                                                float *out_row, float v_scale, int tid,
                                                MergeLds<HEADS, MBMAX> &m)
@@ -597,10 +639,20 @@ __device__ __forceinline__ void merge_partials(const float *ws_ml, const float *
     for (int kc = 0; kc < KC; ++kc) {
         const int e = 4 * tid + kc * 4 * NT;
         if (e < HEADS * D) {
-            const float inv = v_scale / m.mden[e / D];
+            const int h = e / D;
+            const float inv = v_scale / m.mden[h];
+            if constexpr (FOLD_NCV > 0) {
+                // folded records: position q = e' * NCV + p of a head holds d = p * EV + e'
+                constexpr int FEV = D / FOLD_NCV;
+                const int q = e - h * D, e1 = q / FOLD_NCV, p = q - e1 * FOLD_NCV;
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                out_row[e + j] = num[kc][j] * inv;
+                for (int j = 0; j < 4; ++j)
+                    out_row[h * D + (p + j) * FEV + e1] = num[kc][j] * inv;
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    out_row[e + j] = num[kc][j] * inv;
+            }
         }
     }
 }

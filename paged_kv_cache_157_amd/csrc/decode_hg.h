@@ -279,7 +279,7 @@ __global__ __launch_bounds__(64 * HPG, 2) void decode_hg_kernel(DecodeArgs a)
         for (int k = 0; k < ndef; ++k) {
             if (!sm.def_last[k])
                 continue;
-            dec::merge_partials<HG, D, NT, MB>(a.ws_ml, a.ws_acc, sm.def_lo[k], sm.def_np[k],
+            dec::merge_partials<HG, D, NT, MB, 0>(a.ws_ml, a.ws_acc, sm.def_lo[k], sm.def_np[k],
                                                a.out + sm.def_out[k], a.v_scale, tid, sm.merge);
             if (tid == 0)
                 a.ws_count[sm.def_pair[k]] = 0;  // leave the counter at zero for the next call
