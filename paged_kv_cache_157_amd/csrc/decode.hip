@@ -305,6 +305,21 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(DecodeArgs a)
             nx = describe(item_n, i_n, base_n);
             issue_q(i_n, nx.g, qbi ^ 1);
         }
+        // the partial slots [lo, hi] of this segment's (sequence, KV head),
+        // worked out now so that the divisions stay off the hand-over
+        const int pair = i * Hkv + g;
+        int lo = 0, hi = 0;
+        if (!direct) {
+            if (PB > 0) {
+                lo = (int)(item - x);
+                hi = lo + n_i - 1;
+            } else {
+                dec::partial_slot_range(base_i + (long long)g * n_i, n_i, R,
+                                        vbase_i + (long long)g * (n_i + ALPHA) + ALPHA, pair, lo, hi);
+            }
+            lo = uniform(lo);
+            hi = uniform(hi);
+        }
 
         // ---- q for this (sequence, KV head), slot s = head (s ^ lane_m) ---
         uint32_t qr[GP][CPL][QW];
@@ -553,39 +568,45 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(DecodeArgs a)
 
         // ---- merge the waves; write the output, or a partial (kept in the
         // folded order) -----------------------------------------------------------
-        // two neighbouring folded positions (pieces p, p + 1 of one element e)
-        // per thread; a fixed trip count lets every LDS read go out at once
-        constexpr int MPAIRS = G * D / 2, MITER = (MPAIRS + NT - 1) / NT;
+        // four neighbouring folded positions (pieces p .. p + 3 of one element
+        // e) per thread: one 16-byte LDS read per wave, one store
+        constexpr int MQ = G * D / 4, MITER = (MQ + NT - 1) / NT;
+        const auto ws_rec = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(a.ws_acc + (int64_t)(direct ? 0 : slot) * G * D), (short)0, G * D * 4, dec::kBufferRsrcWord3);
 #pragma unroll
         for (int it = 0; it < MITER; ++it) {
-            const int f = 2 * (tid + it * NT);
-            if (MPAIRS % NT != 0 && f >= G * D)
+            const int f = 4 * (tid + it * NT);
+            if (MQ % NT != 0 && f >= G * D)
                 break;
             const int h = f / D, q = f - h * D;
             float M = -INFINITY;
 #pragma unroll
             for (int ww = 0; ww < WAVES; ++ww)
                 M = fmaxf(M, sm.msum[ww][0][h]);
-            float A0 = 0.f, A1 = 0.f, Ls = 0.f;
+            float A[4] = {0.f, 0.f, 0.f, 0.f}, Ls = 0.f;
 #pragma unroll
             for (int ww = 0; ww < WAVES; ++ww) {
                 const float m = sm.msum[ww][0][h];
                 const float fw = m == -INFINITY ? 0.f : fast_exp2(m - M);
-                const float *accw = (const float *)&sm.ring[ww][NSTAGE - 1][0];
-                A0 += fw * accw[f];
-                A1 += fw * accw[f + 1];
-                Ls += fw * sm.msum[ww][1][h];
+                const f32x4 v = *(const f32x4 *)((const float *)&sm.ring[ww][NSTAGE - 1][0] + f);
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    A[j] = fmaf(fw, v[j], A[j]);
+                Ls = fmaf(fw, sm.msum[ww][1][h], Ls);
             }
             if (direct) {
-                const int e = q / NCV, p = q - e * NCV;  // columns p * EV + e and (p + 1) * EV + e
+                const int e = q / NCV, p = q - e * NCV;  // columns (p + j) * EV + e
                 float *dst = a.out + ((int64_t)i * Hq + g * G + h) * D + p * EV + e;
                 const float inv = a.v_scale / Ls;
-                dst[0] = A0 * inv;
-                dst[EV] = A1 * inv;
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    dst[j * EV] = A[j] * inv;
             } else {
                 // partials are written and read with device-coherent (L2-bypassing)
                 // accesses, so the hand-over below needs no cache flush
-                coherent_store2(&a.ws_acc[((int64_t)slot * G + h) * D + q], A0, A1);
+                __builtin_amdgcn_raw_buffer_store_b128(
+                    u32x4{__float_as_uint(A[0]), __float_as_uint(A[1]), __float_as_uint(A[2]), __float_as_uint(A[3])},
+                    ws_rec, f * 4, 0, dec::kBufferCoherent);
                 if (q == 0)
                     coherent_store2(&a.ws_ml[((int64_t)slot * G + h) * 2], M, Ls);
             }
@@ -597,15 +618,6 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(DecodeArgs a)
             // for its coherent partial stores to complete before the barrier that
             // precedes the count, and the merger reads them with coherent loads
             // issued after it has seen the final count.
-            const int pair = i * Hkv + g;
-            int lo, hi;
-            if (PB > 0) {
-                lo = (int)(item - x);
-                hi = lo + n_i - 1;
-            } else {
-                dec::partial_slot_range(base_i + (long long)g * n_i, n_i, R,
-                                        vbase_i + (long long)g * (n_i + ALPHA) + ALPHA, pair, lo, hi);
-            }
             wait_vm<0>();
             barrier_lds();
             if (tid == 0)

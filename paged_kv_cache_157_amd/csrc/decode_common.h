@@ -543,7 +543,7 @@ constexpr int kBufferCoherent = 16;
 // sums).
 template <int HEADS, int MBMAX>
 struct MergeLds {
-    float mM[HEADS], mden[HEADS], mfo[HEADS], mf[MBMAX][HEADS];
+    float mden[HEADS], mfo[HEADS], mf[MBMAX][HEADS];
 };
 
 // Log-sum-exp merge of the np partial records [lo, lo + np) of one pair into
@@ -558,7 +558,8 @@ struct MergeLds {
 // one memory round trip per batch.  MB = 8 where no other registers are live,
 // fewer where prefetched blocks occupy them.  Records are read with
 // device-coherent loads (their writers stored them the same way).  Called by
-// every thread of the work-group (it holds work-group barriers).
+// every thread of the work-group (it holds work-group barriers); no thread may
+// still be reading `m` from an earlier call (a barrier between two calls).
 template <int HEADS, int D, int NT, int MB, int FOLD_NCV, int MBMAX>
 __device__ __forceinline__ void merge_partials(const float *ws_ml, const float *ws_acc, int lo, int np,
                                                float *out_row, float v_scale, int tid,
@@ -575,12 +576,10 @@ __device__ __forceinline__ void merge_partials(const float *ws_ml, const float *
 #pragma unroll
         for (int j = 0; j < 4; ++j)
             num[kc][j] = 0.f;
-    if (tid < HEADS) {
-        m.mM[tid] = -INFINITY;
-        m.mden[tid] = 0.f;
-    }
-    __syncthreads();
+    // the running maximum and sum of head `tid` stay in its thread's registers
+    float hM = -INFINITY, hden = 0.f;
     for (int s0 = 0; s0 < np; s0 += MB) {
+        const bool final_batch = s0 + MB >= np;
         u32x4 ac[MB][KC];
 #pragma unroll
         for (int k2 = 0; k2 < MB; ++k2)
@@ -597,13 +596,13 @@ __device__ __forceinline__ void merge_partials(const float *ws_ml, const float *
             for (int k2 = 0; k2 < MB; ++k2)
                 ml[k2] = s0 + k2 < np ? coherent_load2(&ws_ml[((int64_t)(lo + s0 + k2) * HEADS + tid) * 2])
                                       : f32x2{-INFINITY, 0.f};
-            const float M = m.mM[tid];
+            const float M = hM;
             float Mb = M;
 #pragma unroll
             for (int k2 = 0; k2 < MB; ++k2)
                 Mb = fmaxf(Mb, ml[k2][0]);
             const float fo = M == -INFINITY ? 0.f : fast_exp2(M - Mb);
-            float den = m.mden[tid] * fo;
+            float den = hden * fo;
 #pragma unroll
             for (int k2 = 0; k2 < MB; ++k2) {
                 const float f = ml[k2][0] == -INFINITY ? 0.f : fast_exp2(ml[k2][0] - Mb);
@@ -611,8 +610,10 @@ __device__ __forceinline__ void merge_partials(const float *ws_ml, const float *
                 m.mf[k2][tid] = f;
             }
             m.mfo[tid] = fo;
-            m.mM[tid] = Mb;
-            m.mden[tid] = den;
+            hM = Mb;
+            hden = den;
+            if (final_batch)
+                m.mden[tid] = den;
         }
         __syncthreads();
 #pragma unroll
@@ -633,7 +634,8 @@ __device__ __forceinline__ void merge_partials(const float *ws_ml, const float *
                 }
             }
         }
-        __syncthreads();  // the scale factors of the next batch go to the same place
+        if (!final_batch)
+            __syncthreads();  // the scale factors of the next batch go to the same place
     }
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc) {

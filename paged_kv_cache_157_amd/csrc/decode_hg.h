@@ -276,9 +276,13 @@ __global__ __launch_bounds__(64 * HPG, 2) void decode_hg_kernel(DecodeArgs a)
                                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
                                sm.def_np[tid] - 1;
         __syncthreads();
+        bool merged = false;
         for (int k = 0; k < ndef; ++k) {
             if (!sm.def_last[k])
                 continue;
+            if (merged)
+                __syncthreads();  // the previous merge has read its scratch
+            merged = true;
             dec::merge_partials<HG, D, NT, MB, 0>(a.ws_ml, a.ws_acc, sm.def_lo[k], sm.def_np[k],
                                                a.out + sm.def_out[k], a.v_scale, tid, sm.merge);
             if (tid == 0)

@@ -791,7 +791,6 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
 template <int D>
 __global__ __launch_bounds__(256) void prefill_reduce_kernel(PrefillArgs a)
 {
-    typedef __attribute__((ext_vector_type(4))) float f32x4;
     const int64_t rows = a.total_rows * a.num_q_heads;
     const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (e >= rows * (D / 4))
