@@ -207,9 +207,11 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(DecodeArgs a)
     struct Seg {
         int L, n_i, g, x, seg_items, b0, b1, slot;
     };
-    auto describe = [&](long long it, int &si, long long sbase) -> Seg {
+    // (L: sequence si's length when the caller has it, else -1)
+    auto describe = [&](long long it, int &si, long long sbase, int L) -> Seg {
         Seg d;
-        int L = lens_s[si];
+        if (L < 0)
+            L = lens_s[si];
         int n = dec::items_of(L, maxU, PB);
         while (n == 0) {  // cannot happen for the first segment; skip empties
             ++si;
@@ -218,8 +220,8 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(DecodeArgs a)
         }
         d.L = uniform(L > maxL ? maxL : L);
         d.n_i = uniform(n);
-        const long long rel = it - sbase;
-        d.g = uniform((int)(rel / d.n_i));
+        const long long rel = it - sbase;  // < n_i * Hkv: 32-bit division whenever it fits
+        d.g = uniform(rel < (1ll << 32) ? (int)((unsigned)rel / (unsigned)d.n_i) : (int)(rel / d.n_i));
         d.x = uniform((int)(rel - (long long)d.g * d.n_i));
         const int nblk = (d.L + 15) >> 4;
         if (PB > 0) {
@@ -273,7 +275,7 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(DecodeArgs a)
 
     // the first segment's q and each wave's first block go out together;
     // wave 0 then waits for q only
-    Seg sg = describe(item, i, base_i);
+    Seg sg = describe(item, i, base_i, uniform(sm.range.len));  // the scan read the length
     issue_q(i, sg.g, 0);
     bool pre0 = issue_first(i, sg);  // this wave's first block of the segment is already in stage 0
     if (w == 0) {
@@ -302,7 +304,7 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(DecodeArgs a)
         }
         Seg nx = sg;
         if (has_next) {
-            nx = describe(item_n, i_n, base_n);
+            nx = describe(item_n, i_n, base_n, i_n == i ? L : -1);
             issue_q(i_n, nx.g, qbi ^ 1);
         }
         // the partial slots [lo, hi] of this segment's (sequence, KV head),

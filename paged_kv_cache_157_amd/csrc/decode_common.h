@@ -357,6 +357,7 @@ struct Range {
     long long total_v;  // virtual items (0: plain split)
     long long r0, r1;   // this work-group's real items [r0, r1)
     int seq;            // sequence holding item r0 (-1 when the range is empty)
+    int len;            // its context length (0 when the range is empty)
     long long base;     // first item of that sequence
     long long vbase;    // its first virtual item
 };
@@ -424,8 +425,9 @@ __device__ __forceinline__ Range startup_scan(const int32_t *lens, int S, int pa
     const long long T = virt ? totv : tot;
     // position x of the split -> (sequence, its real / virtual starts, first
     // real item at or after x)
-    auto locate = [&](long long x, int &seq, long long &rbase, long long &vbase) -> long long {
+    auto locate = [&](long long x, int &seq, int &len, long long &rbase, long long &vbase) -> long long {
         seq = -1;
+        len = 0;
         rbase = tot;
         vbase = totv;
         if (x >= T)
@@ -443,6 +445,7 @@ __device__ __forceinline__ Range startup_scan(const int32_t *lens, int S, int pa
             if (m) {
                 const int l2 = __builtin_ctzll(m);
                 seq = base + l2;
+                len = __shfl(l, l2);
                 rbase = rc + __shfl(ri - r, l2);
                 vbase = vc + __shfl(vi - v, l2);
                 const int n = items_of(__shfl(l, l2), maxU, PB);
@@ -461,7 +464,7 @@ __device__ __forceinline__ Range startup_scan(const int32_t *lens, int S, int pa
     R.total = tot;
     R.total_v = virt ? totv : 0;
     long long rb1, vb1;
-    int seq1;
+    int seq1, len1;
     if (one_pass) {
         // the prefix sums above, the found lane read with scalar lane reads;
         // 32-bit divisions wherever the operands fit (T * W < 2^31: every
@@ -471,8 +474,9 @@ __device__ __forceinline__ Range startup_scan(const int32_t *lens, int S, int pa
         auto div = [&](long long num, long long den) -> long long {
             return d32 ? (long long)((unsigned)num / (unsigned)den) : num / den;
         };
-        auto find = [&](long long x, int &seq, long long &rbase, long long &vbase) -> long long {
+        auto find = [&](long long x, int &seq, int &len, long long &rbase, long long &vbase) -> long long {
             seq = -1;
+            len = 0;
             rbase = tot;
             vbase = totv;
             if (x >= T)
@@ -481,6 +485,7 @@ __device__ __forceinline__ Range startup_scan(const int32_t *lens, int S, int pa
             const unsigned long long m = __builtin_amdgcn_ballot_w64(rr0 > 0 && ex <= x && x < in);
             const int l2 = __builtin_ctzll(m);  // m != 0 while x < T
             seq = l2;
+            len = __builtin_amdgcn_readlane(l0, l2);
             rbase = __builtin_amdgcn_readlane(ri0, l2) - __builtin_amdgcn_readlane((int)rr0, l2);
             vbase = __builtin_amdgcn_readlane(vi0, l2) - __builtin_amdgcn_readlane((int)vv0, l2);
             if (!virt)
@@ -490,11 +495,11 @@ __device__ __forceinline__ Range startup_scan(const int32_t *lens, int S, int pa
             const long long gq = div(rel, nn + ALPHA), xv = rel - gq * (nn + ALPHA);
             return rbase + gq * nn + (xv > ALPHA ? xv - ALPHA : 0);
         };
-        R.r0 = find(div(T * blockIdx.x, W), R.seq, R.base, R.vbase);
-        R.r1 = find(div(T * (blockIdx.x + 1), W), seq1, rb1, vb1);
+        R.r0 = find(div(T * blockIdx.x, W), R.seq, R.len, R.base, R.vbase);
+        R.r1 = find(div(T * (blockIdx.x + 1), W), seq1, len1, rb1, vb1);
     } else {
-        R.r0 = locate(T * blockIdx.x / W, R.seq, R.base, R.vbase);
-        R.r1 = locate(T * (blockIdx.x + 1) / W, seq1, rb1, vb1);
+        R.r0 = locate(T * blockIdx.x / W, R.seq, R.len, R.base, R.vbase);
+        R.r1 = locate(T * (blockIdx.x + 1) / W, seq1, len1, rb1, vb1);
     }
     return R;
 }

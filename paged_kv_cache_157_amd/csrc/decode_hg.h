@@ -170,8 +170,8 @@ __global__ __launch_bounds__(64 * HPG, 2) void decode_hg_kernel(DecodeArgs a)
         }
         d.L = uniform(L > maxU * 16 ? maxU * 16 : L);
         d.n_i = uniform(n);
-        const long long rel = it - sbase;
-        d.hg = uniform((int)(rel / d.n_i));
+        const long long rel = it - sbase;  // 32-bit division whenever it fits
+        d.hg = uniform(rel < (1ll << 32) ? (int)((unsigned)rel / (unsigned)d.n_i) : (int)(rel / d.n_i));
         d.x = uniform((int)(rel - (long long)d.hg * d.n_i));
         const int nblk = (d.L + 15) >> 4;
         if (PB > 0) {
@@ -296,7 +296,7 @@ __global__ __launch_bounds__(64 * HPG, 2) void decode_hg_kernel(DecodeArgs a)
     // a load also waits for every load issued before it), then its first two
     // blocks into slots 0 and 1 (the segment's first block again in slot 1 when
     // it has only one: a null block, see below)
-    Seg sg = describe(item, i, base_i, lens_s[i]);
+    Seg sg = describe(item, i, base_i, uniform(sm.range.len));  // the scan read the length
     load_q(i, sg.hg * HPG + w);
     store_q();
     {
