@@ -533,6 +533,10 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(DecodeArgs a)
             __builtin_amdgcn_wave_barrier();
         }
 
+        // ---- the hand-over runs at the highest issue priority (the next
+        // block's step sets the wave's own again)
+        __builtin_amdgcn_s_setprio(3);
+        prio.cur = 3;
         // ---- the following segment's first block goes out now, so its load
         // overlaps this segment's hand-over below (stage 0 is free: this
         // wave's blocks are consumed; the accumulators use the last stage)

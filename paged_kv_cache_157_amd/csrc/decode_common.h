@@ -205,20 +205,18 @@ __device__ __forceinline__ void fold_totals(const float (&acc)[G][EV], float (&o
 {
     constexpr int V = G * EV, H = V / 2, Q = V / 4;
     static_assert(V % 4 == 0, "fold needs a multiple of 4 elements");
-    float t[H];
-#pragma unroll
-    for (int k = 0; k < H; ++k) {
-        // rows 0-1 end with element k, rows 2-3 with element k + H
+    // rows 0-1 end with element k, rows 2-3 with element k + H
+    auto halves = [&](int k) -> float {
         const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[k / EV][k % EV]),
                                                         __float_as_uint(acc[(k + H) / EV][(k + H) % EV]),
                                                         false, false);
-        t[k] = __uint_as_float(s[0]) + __uint_as_float(s[1]);
-    }
+        return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+    };
 #pragma unroll
     for (int k = 0; k < Q; ++k) {
         // row 0: element k, row 1: k + Q, row 2: k + 2Q, row 3: k + 3Q
-        const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(t[k]), __float_as_uint(t[k + Q]), false,
-                                                        false);
+        const float t0 = halves(k), t1 = halves(k + Q);
+        const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(t0), __float_as_uint(t1), false, false);
         float x = __uint_as_float(s[0]) + __uint_as_float(s[1]);
         if constexpr (VTPR == 2)
             x += dpp<DPP_ROW_ROR8>(x);
