@@ -787,8 +787,9 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
     }
 }
 
-// Merge of the key-range splits: thread = (query row, 4 consecutive d).
-template <int D>
+// Merge of the key-range splits: thread = (query row, 4 consecutive d); the
+// loads of all KS splits go out together.
+template <int D, int KS>
 __global__ __launch_bounds__(256) void prefill_reduce_kernel(PrefillArgs a)
 {
     const int64_t rows = a.total_rows * a.num_q_heads;
@@ -797,17 +798,24 @@ __global__ __launch_bounds__(256) void prefill_reduce_kernel(PrefillArgs a)
         return;
     const int64_t qrow = e / (D / 4);
     const int d4 = (int)(e - qrow * (D / 4)) * 4;
-    const int KS = a.kv_splits;
+    f32x2 ml[KS];
+    f32x4 acc[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+        ml[s] = *(const f32x2 *)&a.ws_ml[(s * rows + qrow) * 2];
+        acc[s] = *(const f32x4 *)&a.ws_acc[(s * rows + qrow) * D + d4];
+    }
     float M = -INFINITY;
+#pragma unroll
     for (int s = 0; s < KS; ++s)
-        M = fmaxf(M, a.ws_ml[(s * rows + qrow) * 2]);
+        M = fmaxf(M, ml[s][0]);
     f32x4 num = f32x4{0.f, 0.f, 0.f, 0.f};
     float den = 0.f;
+#pragma unroll
     for (int s = 0; s < KS; ++s) {
-        const f32x2 ml = *(const f32x2 *)&a.ws_ml[(s * rows + qrow) * 2];
-        const float f = ml[0] == -INFINITY ? 0.f : fast_exp2(ml[0] - M);
-        num += f * *(const f32x4 *)&a.ws_acc[(s * rows + qrow) * D + d4];
-        den += f * ml[1];
+        const float f = ml[s][0] == -INFINITY ? 0.f : fast_exp2(ml[s][0] - M);
+        num += f * acc[s];
+        den += f * ml[s][1];
     }
     const float inv = a.v_scale / den;
     float *dst = a.out + qrow * D + d4;
@@ -842,6 +850,18 @@ int prefill_kv_splits(int64_t total_rows, int num_q_heads, int cus)
     return (int)ks;
 }
 
+// the merge instance for the call's split count (2..16)
+template <int D, int KS = 2>
+static void launch_reduce(const PrefillArgs &a, hipStream_t stream)
+{
+    if constexpr (KS <= 16) {
+        if (a.kv_splits != KS)
+            return launch_reduce<D, KS + 1>(a, stream);
+        const int64_t n = a.total_rows * a.num_q_heads * (D / 4);
+        prefill_reduce_kernel<D, KS><<<(unsigned)((n + 255) / 256), 256, 0, stream>>>(a);
+    }
+}
+
 template <int CDT, int D>
 static hipError_t launch_prefill_t(const PrefillArgs &a, hipStream_t stream)
 {
@@ -850,8 +870,7 @@ static hipError_t launch_prefill_t(const PrefillArgs &a, hipStream_t stream)
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.kv_splits == 1)
         return e;
-    const int64_t n = a.total_rows * a.num_q_heads * (D / 4);
-    prefill_reduce_kernel<D><<<(unsigned)((n + 255) / 256), 256, 0, stream>>>(a);
+    launch_reduce<D>(a, stream);
     return hipGetLastError();
 }
 
