@@ -37,6 +37,12 @@
 //   * PV: probabilities go through a 512-byte LDS buffer to the lanes holding
 //     V; each lane owns one 16-byte chunk of V for four tokens of the block
 //     and accumulates G fp32 heads with FMA.
+//   * Segment end: each wave sums its accumulators over the four 16-lane rows
+//     with a reduce-scatter of lane swaps (fold_totals: a quarter of the swaps
+//     and adds of a per-element sum) and stages them in LDS in that folded
+//     order; every thread then merges four positions of the four waves and
+//     writes them to the output, or to the partial record, which keeps the
+//     folded order until the final merge maps it back to columns.
 #include "decode_common.h"
 
 namespace pa {
