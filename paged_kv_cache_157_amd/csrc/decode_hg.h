@@ -81,6 +81,7 @@ __global__ __launch_bounds__(64 * HPG, 2) void decode_hg_kernel(DecodeArgs a)
     using C = dec::DecodeCfg<CDT, D, G, CDT == DT_FP8 ? 8 : 16>;
     using SM = DecodeSmem<CDT, D, G, HPG>;
     constexpr int WAVES = HPG;
+    constexpr bool HG_FOLD = G <= 4;  // partial records in the folded order
     constexpr int NT = 64 * WAVES;
     constexpr int LPT = C::LPT, GP = C::GP, CPL = C::CPL, ROUNDS = C::ROUNDS;
     constexpr int E = C::E, EV = C::EV, NCV = C::NCV, VTPR = C::VTPR, VPASS = C::VPASS, QW = C::QW;
@@ -283,7 +284,7 @@ __global__ __launch_bounds__(64 * HPG, 2) void decode_hg_kernel(DecodeArgs a)
             if (merged)
                 __syncthreads();  // the previous merge has read its scratch
             merged = true;
-            dec::merge_partials<HG, D, NT, MB, 0>(a.ws_ml, a.ws_acc, sm.def_lo[k], sm.def_np[k],
+            dec::merge_partials<HG, D, NT, MB, HG_FOLD ? NCV : 0>(a.ws_ml, a.ws_acc, sm.def_lo[k], sm.def_np[k],
                                                a.out + sm.def_out[k], a.v_scale, tid, sm.merge);
             if (tid == 0)
                 a.ws_count[sm.def_pair[k]] = 0;  // leave the counter at zero for the next call
@@ -511,13 +512,23 @@ __global__ __launch_bounds__(64 * HPG, 2) void decode_hg_kernel(DecodeArgs a)
         }
 
         // ---- this wave's totals for its head -> output or partial -----------
-        // sum over rows and over the lanes of a row that hold other tokens
+        // Up to four heads per KV head the accumulators are summed over rows
+        // by fold_totals (register k of a lane in row r then holds element
+        // j = r * Q + k, j = h * EV + e, and the record keeps that folded
+        // order); with more heads the per-element sums leave every lane of a
+        // row with all totals (the fold's registers do not fit there).
         const float ls = dec::token_total<LPT>(lane_owner ? lsum : 0.f);
+        constexpr int Q = HG_FOLD ? G * EV / 4 : 1;
+        float tot[Q];
+        if constexpr (HG_FOLD) {
+            dec::fold_totals<G, EV, VTPR>(acc, tot);
+        } else {
 #pragma unroll
-        for (int h = 0; h < G; ++h)
+            for (int h = 0; h < G; ++h)
 #pragma unroll
-            for (int e = 0; e < EV; ++e)
-                acc[h][e] = dec::piece_total<VTPR>(acc[h][e]);
+                for (int e = 0; e < EV; ++e)
+                    acc[h][e] = dec::piece_total<VTPR>(acc[h][e]);
+        }
         if (lane < 16 && tr == 0 && lane_owner)
             sm.lsum[w][lane_m] = ls;
         __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
@@ -526,9 +537,18 @@ __global__ __launch_bounds__(64 * HPG, 2) void decode_hg_kernel(DecodeArgs a)
 #pragma unroll
         for (int h = 0; h < G; ++h)
             Lh[h] = sm.lsum[w][h];
-        // lanes < NCV hold piece `lane` (EV elements) of every head's row
+        const int pc = lane & 15, rw = lane >> 4;
         if (direct) {
-            if (lane < NCV) {
+            if constexpr (HG_FOLD) {
+                if (pc < NCV) {
+#pragma unroll
+                    for (int k = 0; k < Q; ++k) {
+                        const int j = rw * Q + k, h = j / EV, e = j - h * EV;
+                        a.out[((int64_t)i * Hq + g * G + h) * D + pc * EV + e] = tot[k] * (a.v_scale / Lh[h]);
+                    }
+                }
+            } else if (lane < NCV) {
+                // lanes < NCV hold piece `lane` (EV elements) of every head's row
 #pragma unroll
                 for (int h = 0; h < G; ++h) {
                     float *dst = a.out + ((int64_t)i * Hq + g * G + h) * D + lane * EV;
@@ -540,7 +560,14 @@ __global__ __launch_bounds__(64 * HPG, 2) void decode_hg_kernel(DecodeArgs a)
             }
         } else {
             const int64_t rec = (int64_t)slot * HPG + w;  // this head's partial record
-            if (lane < NCV) {
+            if constexpr (HG_FOLD) {
+                // element (h, e) of piece p at h * D + e * NCV + p
+                if (pc < NCV) {
+#pragma unroll
+                    for (int k = 0; k < Q; ++k)
+                        coherent_store(&a.ws_acc[(rec * G) * D + (rw * Q + k) * NCV + pc], tot[k]);
+                }
+            } else if (lane < NCV) {
 #pragma unroll
                 for (int h = 0; h < G; ++h)
 #pragma unroll
